@@ -1,0 +1,182 @@
+/*
+ * tq.h -- C ABI of the TurboQuant KV-cache library (libtq.so), MI355X / gfx950.
+ *
+ * The method (pages cited by site and section):
+ *  - Encode [admirer.cn memory-wall article, section 2, stage one]: each key or
+ *    value vector is rotated by one seeded Haar-random orthogonal matrix, its
+ *    length is stored, and every rotated coordinate is quantized by a pure
+ *    threshold lookup into a Lloyd-Max codebook precomputed for the known law
+ *    of a rotated unit vector's coordinates -- no scale, no zero point.
+ *  - Keys add [same article, stage two; intelliparadigm "3-bit" article,
+ *    section 2.1.2] a 1-bit QJL sketch z = [S r > 0] of the quantization
+ *    residual r, with S an m x d Gaussian matrix, so that the inner product
+ *    estimate becomes unbiased.
+ *  - Decode [cc-newplayer explainer, technical breakdown items 2 and 4]: the
+ *    query stays uncompressed; it is rotated once, scored against the packed
+ *    codes plus the QJL correction, softmax-ed, and the dequantized values are
+ *    summed in the rotated domain and rotated back once.
+ *
+ * Conventions shared by every call:
+ *  - d = head_dim, b' = mse_bits (bits per rotated coordinate), L = 2^b',
+ *    m = qjl_dim (0 for values and for MSE-only keys).
+ *  - Rotation: y = Pi x (Pi row-major d x d).  QJL: p = S r (S row-major m x d).
+ *  - Packed codes: code j of a vector occupies bits [j*b', (j+1)*b') of the
+ *    vector's bit stream, least significant bit first; stream bit k is bit
+ *    k%32 of little-endian uint32 word k/32.  A vector has d*b'/32 code words.
+ *    Sign bit i (= [p_i > 0]) is stream bit i of the vector's m/32 sign words.
+ *  - Cache layout (structure of arrays, all device memory, row-major):
+ *      codes[B][H_kv][t_cap][d*b'/32]  uint32
+ *      signs[B][H_kv][t_cap][m/32]     uint32   (keys with m > 0 only)
+ *      norms[B][H_kv][t_cap]           float    nu = ||x||
+ *      res_norms[B][H_kv][t_cap]       float    gamma = ||r|| (keys, m > 0)
+ *    Row index of (b, h, t) is (b*H_kv + h)*t_cap + t.
+ *  - `stream` is a hipStream_t of the codebook's device (NULL = its default
+ *    stream).  Encode and decode only enqueue work: they return before the GPU
+ *    finishes, and a device fault shows up at the caller's next synchronization.
+ *  - Ownership: the caller owns every buffer passed in; the library owns only
+ *    the codebook handle (host tables + one device table buffer).  Encode and
+ *    decode allocate nothing.
+ *  - Errors: every argument is validated on the host before any HIP call; a
+ *    failed check returns a negative status and enqueues nothing.
+ *    tq_last_error() returns a message for the calling thread's last failure.
+ *  - Thread safety: all calls are reentrant; a codebook is immutable after
+ *    build and may be shared by threads and streams.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1, /* bad pointer, size, alignment or combination      */
+  TQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. d != 128 on GPU) */
+  TQ_ERR_ALLOC = -3,       /* host or device allocation failed (build only)    */
+  TQ_ERR_DEVICE = -4       /* a HIP call or kernel launch failed               */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+typedef struct tq_codebook tq_codebook; /* opaque */
+
+/* Build the setup tables once [memory-wall article §2 stage one: the codebooks
+ * are computed ahead of time and stored; inference only looks them up].
+ *   head_dim   d >= 2 (host-only mode); the GPU path supports d == 128.
+ *   mse_bits   b' in 1..4.
+ *   qjl_dim    m: 0 (no QJL) or a multiple of 32; the GPU path supports 0 or 128.
+ *   rot_seed   seed of the Haar rotation's Gaussian matrix.
+ *   qjl_seed   seed of S (ignored when m == 0).
+ *   device     HIP device ordinal, or -1 for a host-only handle (export works,
+ *              encode/decode return TQ_ERR_INVALID_ARG).
+ *   out        receives the handle; free it with tq_codebook_free.
+ * Tables: Lloyd-Max centroids of the density f_d(t) ~ (1-t^2)^((d-3)/2) on
+ * [-1,1] (symmetric; iterated in double to a 1e-13 fixed point) rounded to
+ * fp32, thresholds = fp32 of the midpoints; Pi = Q diag(sign(diag R)) of the
+ * Householder QR of a d x d Gaussian matrix; S = m x d Gaussian.  Gaussians
+ * come from SplitMix64 (state = seed) turned into Box-Muller pairs (cos first),
+ * filled row-major; see DESIGN notes in the source for the exact definition. */
+tq_status tq_codebook_build(int32_t head_dim, int32_t mse_bits, int32_t qjl_dim,
+                            uint64_t rot_seed, uint64_t qjl_seed, int32_t device,
+                            tq_codebook **out);
+
+/* Release a handle (NULL is accepted).  The caller must make sure no enqueued
+ * work still uses it. */
+tq_status tq_codebook_free(tq_codebook *cb);
+
+/* Parameters of a handle; any output pointer may be NULL. */
+tq_status tq_codebook_info(const tq_codebook *cb, int32_t *head_dim, int32_t *mse_bits,
+                           int32_t *qjl_dim, int32_t *device);
+
+/* Copy the host tables out (host pointers; any may be NULL):
+ * centroids[L], thresholds[L-1], rotation[d*d] (row-major, y = Pi x),
+ * qjl[m*d] (row-major; must be NULL when m == 0). */
+tq_status tq_codebook_export(const tq_codebook *cb, float *centroids, float *thresholds,
+                             float *rotation, float *qjl);
+
+/* Same tables in float64 (the values before rounding to fp32). */
+tq_status tq_codebook_export_f64(const tq_codebook *cb, double *centroids, double *thresholds,
+                                 double *rotation, double *qjl);
+
+/* Words per cache row: code_words = d*b'/32, sign_words = m/32 (either may be NULL). */
+tq_status tq_record_words(const tq_codebook *cb, int32_t *code_words, int32_t *sign_words);
+
+/* Encode n vectors online into cache rows [memory-wall article §2: stage one
+ * for all vectors, stage two for keys (m > 0)].
+ *   x             device, n rows of d elements of x_dtype, row r at x + r*x_row_stride
+ *                 elements (x_row_stride >= d; 16-byte aligned rows).
+ *   dst_row       device int64[n] giving the cache row of input row i, or NULL
+ *                 for row i -> cache row i.  Rows whose destination lies outside
+ *                 [0, cache_rows) are skipped (nothing written).
+ *   cache_rows    number of rows the output arrays hold (>= n when dst_row == NULL).
+ *   codes         device uint32[cache_rows][d*b'/32].
+ *   signs         device uint32[cache_rows][m/32]; NULL iff m == 0.
+ *   norms         device float[cache_rows]: nu = ||x||.
+ *   res_norms     device float[cache_rows]: gamma = ||y - c[idx]||; NULL iff m == 0.
+ *   dbg_rot       NULL, or device float[n][d]: the rotated unit vector y = Pi x/nu
+ *                 exactly as quantized (indexed by input row).
+ *   dbg_proj      NULL, or device float[n][m]: p = S r exactly as signed (m > 0).
+ * Per vector: nu = ||x||; y = Pi x / nu (y = 0 when nu == 0); code_j =
+ * #{i : y_j >= t_i} (NaN -> 0); keys: r = y - c[code], gamma = ||r||,
+ * sign_i = [ (S r)_i > 0 ].  Pure function of (x, codebook): re-running it on
+ * the same rows is idempotent.  n == 0 is a no-op. */
+tq_status tq_encode_kv(const tq_codebook *cb, const void *x, tq_dtype x_dtype, int64_t n,
+                       int64_t x_row_stride, const int64_t *dst_row, int64_t cache_rows,
+                       uint32_t *codes, uint32_t *signs, float *norms, float *res_norms,
+                       float *dbg_rot, float *dbg_proj, void *stream);
+
+/* One compressed cache tensor set, laid out as described at the top. */
+typedef struct {
+  const uint32_t *codes;
+  const uint32_t *signs;     /* keys with m > 0, else NULL */
+  const float *norms;
+  const float *res_norms;    /* keys with m > 0, else NULL */
+  int64_t t_cap;             /* tokens per (batch, kv head) row block */
+} tq_cache;
+
+/* Bytes of device workspace tq_decode_attention needs for these sizes. */
+tq_status tq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int64_t t_cap, size_t *bytes);
+
+/* Single-query decode attention over the compressed cache [cc-newplayer
+ * explainer item 4: Q uncompressed, attention with dequantization].
+ *   kcb, vcb      key codebook (its Pi, S, centroids) and value codebook
+ *                 (vcb->m must be 0); both on the same device, same d.
+ *   q             device [batch][n_q_heads][d] of q_dtype (contiguous).
+ *   k, v          host structs holding device pointers; k->t_cap == v->t_cap.
+ *   seq_len       device int32[batch]: tokens to attend per sequence; values are
+ *                 clamped to [0, t_cap].
+ *   n_q_heads     multiple of n_kv_heads; q head h reads kv head h / (H_q/H_kv).
+ *   softmax_scale <= 0 selects 1/sqrt(d).
+ *   out           device [batch][n_q_heads][d] of out_dtype; a sequence with
+ *                 seq_len 0 gets zeros.  bf16 output is the round-to-nearest-even
+ *                 of the fp32 result.
+ *   dbg_scores    NULL or device float[batch][n_q_heads][t_cap]: the scaled
+ *                 logits l_t for t < seq_len (other entries untouched).
+ *   workspace     device buffer of at least tq_decode_workspace_bytes bytes,
+ *                 256-byte aligned; its contents on entry do not matter.
+ * Score: l_t = scale * nu_t * ( <Pi q, c_k[code_t]> + sqrt(pi/2)/m * gamma_t *
+ * <S Pi q, 2 z_t - 1> ); output o = Pi_v^T sum_t softmax(l)_t nu^v_t c_v[code^v_t].
+ * Deterministic: the same inputs give bitwise-identical outputs. */
+tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, const void *q,
+                              tq_dtype q_dtype, const tq_cache *k, const tq_cache *v,
+                              const int32_t *seq_len, int32_t batch, int32_t n_q_heads,
+                              int32_t n_kv_heads, float softmax_scale, void *out,
+                              tq_dtype out_dtype, float *dbg_scores, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Static name of a status code. */
+const char *tq_status_string(tq_status s);
+
+/* Message describing the calling thread's most recent failed call ("" if none). */
+const char *tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,365 @@
+// C-ABI layer of libtq.so: argument validation, codebook handles, device
+// tables and kernel launches.  Declarations and contracts: include/tq.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "tq.h"
+#include "tq_internal.h"
+#include "tq_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tq_status fail(tq_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+tq_status ok() {
+  return TQ_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Switches to `device` for the lifetime of the guard, restoring the caller's.
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int device) {
+    err = hipGetDevice(&prev);
+    if (err != hipSuccess) return;
+    if (prev != device) {
+      err = hipSetDevice(device);
+      changed = (err == hipSuccess);
+    }
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+int cu_count(int device) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  if (device >= static_cast<int>(cache.size())) cache.resize(device + 1, 0);
+  if (cache[device] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || v <= 0) v = 256;
+    cache[device] = v;
+  }
+  return cache[device];
+}
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+tq_status upload_tables(tq_codebook *cb) {
+  const tq::HostTables &h = cb->host;
+  const int d = h.d, m = h.m;
+  // Device tables are only built for the GPU path's shape.
+  size_t off = 0;
+  cb->off_centroids = off;
+  off = align256(off + tq::kMaxLevels * sizeof(float));
+  cb->off_thresholds = off;
+  off = align256(off + tq::kMaxLevels * sizeof(float));
+  cb->off_rot_frag = off;
+  off = align256(off + tq::kFragBytes);
+  cb->off_qjl_frag = off;
+  off = align256(off + (m > 0 ? tq::kFragBytes : 0));
+  cb->off_rot_f32 = off;
+  off = align256(off + static_cast<size_t>(d) * d * sizeof(float));
+  cb->off_rot_t_f32 = off;
+  off = align256(off + static_cast<size_t>(d) * d * sizeof(float));
+  cb->off_qjl_f32 = off;
+  off = align256(off + static_cast<size_t>(m) * d * sizeof(float));
+  cb->off_qjl_t_f32 = off;
+  off = align256(off + static_cast<size_t>(m) * d * sizeof(float));
+  cb->dev_bytes = off;
+
+  std::vector<unsigned char> img(off, 0);
+  std::memcpy(img.data() + cb->off_centroids, h.centroids.data(), h.centroids.size() * sizeof(float));
+  std::memcpy(img.data() + cb->off_thresholds, h.thresholds.data(), h.thresholds.size() * sizeof(float));
+  tq::pack_encode_fragments(h.rotation.data(), img.data() + cb->off_rot_frag);
+  if (m > 0) tq::pack_encode_fragments(h.qjl.data(), img.data() + cb->off_qjl_frag);
+  std::memcpy(img.data() + cb->off_rot_f32, h.rotation.data(), h.rotation.size() * sizeof(float));
+  float *rt = reinterpret_cast<float *>(img.data() + cb->off_rot_t_f32);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) rt[i * d + j] = h.rotation[static_cast<size_t>(j) * d + i];
+  if (m > 0) {
+    std::memcpy(img.data() + cb->off_qjl_f32, h.qjl.data(), h.qjl.size() * sizeof(float));
+    float *st = reinterpret_cast<float *>(img.data() + cb->off_qjl_t_f32);
+    for (int i = 0; i < d; ++i)
+      for (int r = 0; r < m; ++r) st[i * m + r] = h.qjl[static_cast<size_t>(r) * d + i];
+  }
+  DeviceGuard guard(cb->device);
+  if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice(%d): %s", cb->device, hipGetErrorString(guard.err));
+  hipError_t e = hipMalloc(&cb->dev_buf, off);
+  if (e != hipSuccess) {
+    cb->dev_buf = nullptr;
+    return fail(TQ_ERR_ALLOC, "hipMalloc(%zu): %s", off, hipGetErrorString(e));
+  }
+  e = hipMemcpy(cb->dev_buf, img.data(), off, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "hipMemcpy: %s", hipGetErrorString(e));
+  return ok();
+}
+
+template <typename T>
+const T *dev_ptr(const tq_codebook *cb, size_t off) {
+  return reinterpret_cast<const T *>(static_cast<const unsigned char *>(cb->dev_buf) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_codebook_build(int32_t head_dim, int32_t mse_bits, int32_t qjl_dim, uint64_t rot_seed,
+                            uint64_t qjl_seed, int32_t device, tq_codebook **out) {
+  if (out == nullptr) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (device < -1) return fail(TQ_ERR_INVALID_ARG, "device must be >= -1");
+  if (device >= 0) {
+    if (head_dim != tq::kHeadDim)
+      return fail(TQ_ERR_UNSUPPORTED, "the GPU path supports head_dim 128 only (got %d)", head_dim);
+    if (qjl_dim != 0 && qjl_dim != tq::kQjlDim)
+      return fail(TQ_ERR_UNSUPPORTED, "the GPU path supports qjl_dim 0 or 128 only (got %d)", qjl_dim);
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device >= count)
+      return fail(TQ_ERR_INVALID_ARG, "device %d not present (%d devices)", device, count);
+  }
+  tq_codebook *cb = new (std::nothrow) tq_codebook();
+  if (cb == nullptr) return fail(TQ_ERR_ALLOC, "host allocation failed");
+  std::string err;
+  if (!tq::build_host_tables(head_dim, mse_bits, qjl_dim, rot_seed, qjl_seed, &cb->host, &err)) {
+    delete cb;
+    return fail(TQ_ERR_INVALID_ARG, "%s", err.c_str());
+  }
+  cb->rot_seed = rot_seed;
+  cb->qjl_seed = qjl_seed;
+  cb->device = device;
+  if (device >= 0) {
+    tq_status s = upload_tables(cb);
+    if (s != TQ_OK) {
+      tq_codebook_free(cb);
+      return s;
+    }
+  }
+  *out = cb;
+  return ok();
+}
+
+tq_status tq_codebook_free(tq_codebook *cb) {
+  if (cb == nullptr) return ok();
+  tq_status s = TQ_OK;
+  if (cb->dev_buf != nullptr) {
+    DeviceGuard guard(cb->device);
+    if (hipFree(cb->dev_buf) != hipSuccess) s = fail(TQ_ERR_DEVICE, "hipFree failed");
+  }
+  delete cb;
+  return s;
+}
+
+tq_status tq_codebook_info(const tq_codebook *cb, int32_t *head_dim, int32_t *mse_bits, int32_t *qjl_dim,
+                           int32_t *device) {
+  if (cb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  if (head_dim) *head_dim = cb->host.d;
+  if (mse_bits) *mse_bits = cb->host.bits;
+  if (qjl_dim) *qjl_dim = cb->host.m;
+  if (device) *device = cb->device;
+  return ok();
+}
+
+tq_status tq_codebook_export(const tq_codebook *cb, float *centroids, float *thresholds, float *rotation,
+                             float *qjl) {
+  if (cb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  const tq::HostTables &h = cb->host;
+  if (qjl != nullptr && h.m == 0) return fail(TQ_ERR_INVALID_ARG, "qjl requested but qjl_dim is 0");
+  if (centroids) std::memcpy(centroids, h.centroids.data(), h.centroids.size() * sizeof(float));
+  if (thresholds) std::memcpy(thresholds, h.thresholds.data(), h.thresholds.size() * sizeof(float));
+  if (rotation) std::memcpy(rotation, h.rotation.data(), h.rotation.size() * sizeof(float));
+  if (qjl) std::memcpy(qjl, h.qjl.data(), h.qjl.size() * sizeof(float));
+  return ok();
+}
+
+tq_status tq_codebook_export_f64(const tq_codebook *cb, double *centroids, double *thresholds, double *rotation,
+                                 double *qjl) {
+  if (cb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  const tq::HostTables &h = cb->host;
+  if (qjl != nullptr && h.m == 0) return fail(TQ_ERR_INVALID_ARG, "qjl requested but qjl_dim is 0");
+  if (centroids) std::memcpy(centroids, h.centroids64.data(), h.centroids64.size() * sizeof(double));
+  if (thresholds) std::memcpy(thresholds, h.thresholds64.data(), h.thresholds64.size() * sizeof(double));
+  if (rotation) std::memcpy(rotation, h.rotation64.data(), h.rotation64.size() * sizeof(double));
+  if (qjl) std::memcpy(qjl, h.qjl64.data(), h.qjl64.size() * sizeof(double));
+  return ok();
+}
+
+tq_status tq_record_words(const tq_codebook *cb, int32_t *code_words, int32_t *sign_words) {
+  if (cb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  const int bitsum = cb->host.d * cb->host.bits;
+  if (code_words) *code_words = (bitsum + 31) / 32;
+  if (sign_words) *sign_words = cb->host.m / 32;
+  return ok();
+}
+
+tq_status tq_encode_kv(const tq_codebook *cb, const void *x, tq_dtype x_dtype, int64_t n, int64_t x_row_stride,
+                       const int64_t *dst_row, int64_t cache_rows, uint32_t *codes, uint32_t *signs, float *norms,
+                       float *res_norms, float *dbg_rot, float *dbg_proj, void *stream) {
+  if (cb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  if (cb->device < 0) return fail(TQ_ERR_INVALID_ARG, "host-only codebook cannot encode");
+  const int d = cb->host.d, m = cb->host.m;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "x_dtype must be TQ_F32 or TQ_BF16");
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return ok();
+  if (x == nullptr || codes == nullptr || norms == nullptr) return fail(TQ_ERR_INVALID_ARG, "x, codes and norms are required");
+  if (x_row_stride < d) return fail(TQ_ERR_INVALID_ARG, "x_row_stride (%lld) < head_dim", static_cast<long long>(x_row_stride));
+  const size_t esize = (x_dtype == TQ_F32) ? 4 : 2;
+  if (!aligned(x, 16) || (static_cast<size_t>(x_row_stride) * esize) % 16 != 0)
+    return fail(TQ_ERR_INVALID_ARG, "x and its row stride must be 16-byte aligned");
+  if ((m > 0) != (signs != nullptr) || (m > 0) != (res_norms != nullptr))
+    return fail(TQ_ERR_INVALID_ARG, "signs and res_norms must be given iff qjl_dim > 0");
+  if (dbg_proj != nullptr && m == 0) return fail(TQ_ERR_INVALID_ARG, "dbg_proj needs qjl_dim > 0");
+  if (cache_rows < 0 || (dst_row == nullptr && cache_rows < n))
+    return fail(TQ_ERR_INVALID_ARG, "cache_rows (%lld) too small for n (%lld)", static_cast<long long>(cache_rows),
+                static_cast<long long>(n));
+  if (!aligned(codes, 4) || !aligned(norms, 4) || (signs && !aligned(signs, 4)) || (res_norms && !aligned(res_norms, 4)) ||
+      (dbg_rot && !aligned(dbg_rot, 16)) || (dbg_proj && !aligned(dbg_proj, 16)) || (dst_row && !aligned(dst_row, 8)))
+    return fail(TQ_ERR_INVALID_ARG, "misaligned output pointer");
+  tq::EncodeArgs a{};
+  a.x = x;
+  a.x_stride = x_row_stride;
+  a.n = n;
+  a.dst_row = dst_row;
+  a.cache_rows = cache_rows;
+  a.codes = codes;
+  a.signs = signs;
+  a.norms = norms;
+  a.res_norms = res_norms;
+  a.dbg_rot = dbg_rot;
+  a.dbg_proj = dbg_proj;
+  a.frag_rot = dev_ptr<uint4>(cb, cb->off_rot_frag);
+  a.frag_qjl = (m > 0) ? dev_ptr<uint4>(cb, cb->off_qjl_frag) : nullptr;
+  for (int i = 0; i < tq::kMaxLevels; ++i) {
+    a.centroids[i] = i < cb->host.levels ? cb->host.centroids[i] : 0.f;
+    a.thresholds[i] = i < cb->host.levels - 1 ? cb->host.thresholds[i] : INFINITY;
+  }
+  DeviceGuard guard(cb->device);
+  if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
+  hipError_t e = tq::launch_encode(a, cb->host.bits, m > 0, x_dtype == TQ_F32, cu_count(cb->device),
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "encode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+tq_status tq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t t_cap,
+                                    size_t *bytes) {
+  if (bytes == nullptr) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || t_cap < 1 || n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d/%d, t_cap %lld)", batch, n_q_heads, n_kv_heads,
+                static_cast<long long>(t_cap));
+  *bytes = tq::plan_decode(batch, n_q_heads, n_kv_heads, t_cap).total_bytes;
+  return ok();
+}
+
+tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
+                              const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
+                              int32_t n_q_heads, int32_t n_kv_heads, float softmax_scale, void *out,
+                              tq_dtype out_dtype, float *dbg_scores, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  if (kcb == nullptr || vcb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  if (kcb->device < 0 || vcb->device != kcb->device)
+    return fail(TQ_ERR_INVALID_ARG, "codebooks must live on the same GPU device");
+  if (kcb->host.d != vcb->host.d) return fail(TQ_ERR_INVALID_ARG, "key and value head_dim differ");
+  if (vcb->host.m != 0) return fail(TQ_ERR_INVALID_ARG, "the value codebook must have qjl_dim 0");
+  if (q == nullptr || k == nullptr || v == nullptr || seq_len == nullptr || out == nullptr || workspace == nullptr)
+    return fail(TQ_ERR_INVALID_ARG, "NULL argument");
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad q_dtype");
+  if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad out_dtype");
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d/%d)", batch, n_q_heads, n_kv_heads);
+  const int g = n_q_heads / n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+    return fail(TQ_ERR_UNSUPPORTED, "q heads per kv head must be 1, 2, 4, 8 or 16 (got %d)", g);
+  if (k->t_cap < 1 || v->t_cap != k->t_cap) return fail(TQ_ERR_INVALID_ARG, "key/value t_cap must match and be >= 1");
+  if (k->t_cap > (int64_t{1} << 30)) return fail(TQ_ERR_UNSUPPORTED, "t_cap above 2^30");
+  const int m = kcb->host.m;
+  if (k->codes == nullptr || k->norms == nullptr || v->codes == nullptr || v->norms == nullptr)
+    return fail(TQ_ERR_INVALID_ARG, "cache codes/norms are required");
+  if ((m > 0) != (k->signs != nullptr) || (m > 0) != (k->res_norms != nullptr))
+    return fail(TQ_ERR_INVALID_ARG, "key signs/res_norms must be given iff the key codebook has qjl_dim > 0");
+  if (!aligned(k->codes, 16) || !aligned(v->codes, 16) || (k->signs && !aligned(k->signs, 16)) ||
+      !aligned(k->norms, 4) || !aligned(v->norms, 4) || !aligned(q, 4) || !aligned(out, 4) || !aligned(workspace, 256) ||
+      !aligned(seq_len, 4) || (dbg_scores && !aligned(dbg_scores, 4)))
+    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer");
+  const tq::DecodePlan plan = tq::plan_decode(batch, n_q_heads, n_kv_heads, k->t_cap);
+  if (workspace_bytes < plan.total_bytes)
+    return fail(TQ_ERR_INVALID_ARG, "workspace too small (%zu < %zu)", workspace_bytes, plan.total_bytes);
+  tq::DecodeArgs a{};
+  a.q = q;
+  a.q_bf16 = (q_dtype == TQ_BF16);
+  a.k_codes = k->codes;
+  a.k_signs = k->signs;
+  a.k_norms = k->norms;
+  a.k_res = k->res_norms;
+  a.v_codes = v->codes;
+  a.v_norms = v->norms;
+  a.t_cap = k->t_cap;
+  a.seq_len = seq_len;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.k_bits = kcb->host.bits;
+  a.v_bits = vcb->host.bits;
+  a.qjl_m = m;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(kcb->host.d));
+  a.qjl_coef = m > 0 ? static_cast<float>(std::sqrt(3.14159265358979323846 / 2.0) / m) : 0.f;
+  a.out = out;
+  a.out_bf16 = (out_dtype == TQ_BF16);
+  a.dbg_scores = dbg_scores;
+  a.rot_k_t = dev_ptr<float>(kcb, kcb->off_rot_t_f32);
+  a.qjl_t = m > 0 ? dev_ptr<float>(kcb, kcb->off_qjl_t_f32) : nullptr;
+  a.rot_v = dev_ptr<float>(vcb, vcb->off_rot_f32);
+  for (int i = 0; i < tq::kMaxLevels; ++i) {
+    a.k_centroids[i] = i < kcb->host.levels ? kcb->host.centroids[i] : 0.f;
+    a.v_centroids[i] = i < vcb->host.levels ? vcb->host.centroids[i] : 0.f;
+  }
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  a.ws_qprep = reinterpret_cast<float *>(ws + plan.off_qprep);
+  a.ws_part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
+  a.ws_part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
+  a.chunk = plan.chunk;
+  a.n_chunks = plan.n_chunks;
+  DeviceGuard guard(kcb->device);
+  if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
+  hipError_t e = tq::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char *tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+    case TQ_ERR_ALLOC: return "TQ_ERR_ALLOC";
+    case TQ_ERR_DEVICE: return "TQ_ERR_DEVICE";
+  }
+  return "TQ_UNKNOWN_STATUS";
+}
+
+const char *tq_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal declarations shared by the host setup, the C-ABI layer and the
+// kernel launchers of libtq.so.  Not installed; the public ABI is include/tq.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "tq.h"
+
+namespace tq {
+
+// Host-side tables of one codebook handle (all row-major).
+struct HostTables {
+  int d = 0, bits = 0, m = 0, levels = 0;
+  std::vector<double> centroids64, thresholds64, rotation64, qjl64;
+  std::vector<float> centroids, thresholds, rotation, qjl;
+};
+
+// Builds every host table; returns false (with `err` set) on bad input.
+bool build_host_tables(int d, int bits, int m, uint64_t rot_seed, uint64_t qjl_seed,
+                       HostTables *out, std::string *err);
+
+// Pieces exposed for the CPU tests of the library's own setup code.
+double sphere_coord_cdf(double t, int d);
+void lloyd_max_sphere(int d, int bits, std::vector<double> *centroids,
+                      std::vector<double> *thresholds, int *iterations);
+void seeded_normals(uint64_t seed, size_t count, double *out);
+void haar_orthogonal(int d, uint64_t seed, double *pi_rowmajor);
+
+// bf16 round-to-nearest-even of a float, as raw bits.
+uint16_t bf16_bits_rne(float v);
+float bf16_bits_to_float(uint16_t b);
+
+}  // namespace tq
+
+// Device-side part of a codebook handle (owned by the C-ABI layer).
+struct tq_codebook {
+  tq::HostTables host;
+  uint64_t rot_seed = 0, qjl_seed = 0;
+  int device = -1;
+  void *dev_buf = nullptr;        // one hipMalloc holding every device table
+  size_t dev_bytes = 0;
+  // Offsets (bytes) into dev_buf.
+  size_t off_centroids = 0;       // float[L]
+  size_t off_thresholds = 0;      // float[L-1] (padded)
+  size_t off_rot_frag = 0;        // encode A-operand fragments of Pi: hi then lo
+  size_t off_qjl_frag = 0;        // encode A-operand fragments of S: hi then lo
+  size_t off_rot_f32 = 0;         // float[d*d] row-major Pi
+  size_t off_rot_t_f32 = 0;       // float[d*d] row-major Pi^T
+  size_t off_qjl_f32 = 0;         // float[m*d] row-major S
+  size_t off_qjl_t_f32 = 0;       // float[d*m] row-major S^T
+};

@@ -84,14 +84,16 @@ def coord_partial_mean(t, d: int):
 # --------------------------------------------------------------------------
 
 
-def lloyd_max(d: int, bits: int, tol: float = 1e-13, max_iter: int = 200000):
+def lloyd_max(d: int, bits: int, tol: float = 1e-15, max_iter: int = 200000):
     """Lloyd-Max scalar quantizer for f_d with L = 2**bits levels.
 
     The page calls it a one-dimensional continuous k-means on the known
     coordinate law, solved once per bit width and stored.  Steps (Lloyd's
     iteration): thresholds are midpoints of neighbouring centroids; each
     centroid is the conditional mean of its cell.  Reading: start from a
-    symmetric equal-spaced guess, stop when no centroid moves by `tol`.  The
+    symmetric equal-spaced guess, stop when no centroid moves by `tol`
+    (1e-15: the iteration contracts slowly at 4 bits, so a looser stop would
+    leave ~1e-12 of error, enough to move an fp32 rounding).  The
     law is even, so the optimum is symmetric; each step is symmetrized
     (c <- (c - reversed c)/2) so that rounding cannot tilt it and the middle
     threshold is exactly 0.
