@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the TurboQuant KV-cache hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: encode every key
+and value vector of the layer into the compressed cache (two launches), then
+one decode-attention step over a full compressed cache.  Default workload:
+Llama-3-8B-shaped layer, batch 1, 32768 tokens, 32 q heads / 8 KV heads,
+head_dim 128, keys b=3 (2-bit codes + 1-bit QJL, m=128), values 3-bit.
+
+Inputs are resident in HBM before timing.  To keep the 256 MB Infinity Cache
+from serving re-reads, each step reads one of several input replicas and the
+decode reads a cache replica written many steps earlier (>= 1 GiB of distinct
+caches in rotation); --hot disables the rotation.
+
+Prints ONE JSON line.  `value` is the decode-attention throughput in GB/s of
+compressed K+V bytes read; encode throughput (Mvectors/s) and both kernels'
+roofline figures are reported alongside.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "decode-attn HBM GB/s (% of peak) on compressed KV; encode Mvectors/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama8b", choices=["llama8b", "llama70b", "batched2", "batched4"])
+    ap.add_argument("--hot", action="store_true", help="no replica rotation (cache-resident numbers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 18, help="vectors per tensor in the oracle encode sample")
+    return ap.parse_args()
+
+
+def workload(name):
+    from online_vector_quantization_amd import synth
+    if name == "llama8b":
+        return synth.llama8b()
+    if name == "llama70b":
+        return synth.llama70b()
+    if name == "batched2":
+        return synth.batched(2)
+    return synth.batched(4)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import online_vector_quantization_amd as T
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    T.load_library()
+    dev = torch.device("cuda", 0)
+    t0 = time.time()
+    wl = workload(args.config)
+    B, Hq, Hkv, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.seq_len
+    kbits_mse = wl.k_bits - 1
+    print(f"[bench] workload {wl.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    kcb = T.Codebook(128, kbits_mse, 128, 0, 1, device=0)
+    vcb = T.Codebook(128, wl.v_bits, 0, 0, 1, device=0)
+    n_vec = B * Hkv * S
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev).reshape(-1, 128)
+
+    k0, v0 = up(wl.k), up(wl.v)
+    q = torch.from_numpy(np.ascontiguousarray(wl.q).view(np.int16)).view(torch.bfloat16).to(dev)
+    in_bytes = 2 * n_vec * 128 * 2
+    cache_bytes_one = n_vec * T.compressed_bytes_per_token(kcb, vcb)
+    n_in = 1 if args.hot else max(2, math.ceil((512 << 20) / in_bytes))
+    n_cache = 1 if args.hot else max(2, math.ceil((1 << 30) / cache_bytes_one))
+    ins = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(n_in - 1)]
+    caches = [(T.CompressedCache.allocate(kcb, B, Hkv, S), T.CompressedCache.allocate(vcb, B, Hkv, S))
+              for _ in range(n_cache)]
+    seq = torch.full((B,), S, dtype=torch.int32, device=dev)
+    ws = T.alloc_workspace(B, Hq, Hkv, S, dev)
+    out = torch.empty(B, Hq, 128, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def encode(i_in, i_c):
+        kx, vx = ins[i_in]
+        kc, vc = caches[i_c]
+        T.encode_into_cache(kcb, kx, kc, stream=stream)
+        T.encode_into_cache(vcb, vx, vc, stream=stream)
+
+    def decode(i_c):
+        kc, vc = caches[i_c]
+        T.decode_attention(kcb, vcb, q, kc, vc, seq, out=out, workspace=ws, stream=stream)
+
+    # fill every cache replica once (untimed), then warm up
+    for i in range(n_cache):
+        encode(i % n_in, i)
+    for s in range(args.warmup):
+        encode(s % n_in, s % n_cache)
+        decode((s + n_cache // 2) % n_cache)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [(ev(), ev(), ev(), ev()) for _ in range(args.steps)]
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        e0, e1, e2, e3 = marks[s]
+        kx, vx = ins[s % n_in]
+        kc, vc = caches[s % n_cache]
+        e0.record(stream)
+        T.encode_into_cache(kcb, kx, kc, stream=stream)
+        e1.record(stream)
+        T.encode_into_cache(vcb, vx, vc, stream=stream)
+        e2.record(stream)
+        decode((s + n_cache // 2) % n_cache)
+        e3.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    enc_k = np.array([m[0].elapsed_time(m[1]) for m in marks])
+    enc_v = np.array([m[1].elapsed_time(m[2]) for m in marks])
+    dec = np.array([m[2].elapsed_time(m[3]) for m in marks])
+
+    ms_step = total_ms / args.steps
+    dec_ms = float(dec.mean())
+    dec_bytes = cache_bytes_one
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    enc_ms = float((enc_k + enc_v).mean())
+    enc_mvps = 2 * n_vec / (enc_ms * 1e-3) / 1e6
+    k_rec = 4 * kcb.code_words + 4 * kcb.sign_words + 8
+    v_rec = 4 * vcb.code_words + 4
+    enc_k_bytes = n_vec * (256 + k_rec)
+    enc_v_bytes = n_vec * (256 + v_rec)
+    enc_k_gbps = enc_k_bytes / (enc_k.mean() * 1e-3) / 1e9
+    enc_v_gbps = enc_v_bytes / (enc_v.mean() * 1e-3) / 1e9
+    enc_k_tflops = n_vec * 2 * 128 * (128 + 128) / (enc_k.mean() * 1e-3) / 1e12
+
+    line = {
+        "metric": METRIC,
+        "value": round(dec_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
+            "key_bits": wl.k_bits, "value_bits": wl.v_bits, "qjl_dim": 128, "input_dtype": "bf16",
+            "step": "encode all K and V of the layer, then one decode step over a full cache",
+            "cold_replicas": {"inputs": n_in, "caches": n_cache, "hot": bool(args.hot)},
+        },
+        "decode_frac_of_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "decode_us": round(dec_ms * 1e3, 2),
+        "encode_mvectors_per_s": round(enc_mvps, 1),
+        "encode_us": {"keys": round(float(enc_k.mean()) * 1e3, 2), "values": round(float(enc_v.mean()) * 1e3, 2)},
+        "roofline": {
+            "kernel": "encode (keys: rotation + QJL)", "bound": "hbm",
+            "achieved": round(enc_k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": enc_k_bytes, "avg_launch_us": round(float(enc_k.mean()) * 1e3, 2),
+            "mfma_tflops_algorithmic": round(enc_k_tflops, 1),
+        },
+        "roofline_values_encode": {
+            "bound": "hbm", "achieved": round(enc_v_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(enc_v_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": enc_v_bytes,
+            "avg_launch_us": round(float(enc_v.mean()) * 1e3, 2),
+        },
+        "roofline_decode": {
+            "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": dec_bytes,
+            "avg_us_qprep_partial_combine": round(dec_ms * 1e3, 2),
+        },
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, sample):
+    """The CPU oracle (float64 numpy) on a bounded sample of the same workload."""
+    import oracle as O
+    from online_vector_quantization_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    kb = wl.k_bits - 1
+    c_k, t_k = O.build_codebook(128, kb)
+    c_v, t_v = O.build_codebook(128, wl.v_bits)
+    Pi = O.haar_rotation(128, 0)
+    Sm = O.qjl_matrix(128, 128, 1)
+    kx = synth.bf16_to_f32(wl.k.reshape(-1, 128)[:sample])
+    vx = synth.bf16_to_f32(wl.v.reshape(-1, 128)[:sample])
+    t0 = time.perf_counter()
+    ek = O.encode(kx, Pi, c_k, t_k, Sm)
+    k_codes = O.pack_bits(ek["idx"], kb)
+    k_signs = O.pack_bits(ek["z"], 1)
+    ev = O.encode(vx, Pi, c_v, t_v)
+    v_codes = O.pack_bits(ev["idx"], wl.v_bits)
+    t_enc = time.perf_counter() - t0
+    # decode over the encoded sample, viewed as one (batch, kv head) row of `sample` tokens
+    kcache = {"codes": k_codes[None, None], "signs": k_signs[None, None], "norms": ek["nu"][None, None],
+              "res_norms": ek["gamma"][None, None]}
+    vcache = {"codes": v_codes[None, None], "norms": ev["nu"][None, None]}
+    g = wl.n_q_heads // wl.n_kv_heads
+    qh = synth.bf16_to_f32(wl.q[0, :g]).astype(np.float64)[None]
+    t1 = time.perf_counter()
+    O.decode_attention(qh, kcache, vcache, [sample], {"bits": kb, "centroids": c_k, "Pi": Pi, "S": Sm},
+                       {"bits": wl.v_bits, "centroids": c_v, "Pi": Pi})
+    t_dec = time.perf_counter() - t1
+    rec = (4 * 4 * kb + 16 + 8) + (4 * 4 * wl.v_bits + 4)
+    dec_gbps = sample * rec / t_dec / 1e9
+    return {"value": round(dec_gbps, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "encode_mvectors_per_s": round(2 * sample / t_enc / 1e6, 4),
+            "sample": f"first {sample} K and {sample} V vectors of the workload: oracle encode "
+                      f"({t_enc:.2f}s), then oracle decode of {g} q heads over those {sample} tokens "
+                      f"({t_dec:.2f}s); GB/s = compressed bytes read / decode time",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

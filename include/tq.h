@@ -75,7 +75,8 @@ typedef struct tq_codebook tq_codebook; /* opaque */
  *              encode/decode return TQ_ERR_INVALID_ARG).
  *   out        receives the handle; free it with tq_codebook_free.
  * Tables: Lloyd-Max centroids of the density f_d(t) ~ (1-t^2)^((d-3)/2) on
- * [-1,1] (symmetric; iterated in double to a 1e-13 fixed point) rounded to
+ * [-1,1] (symmetric; Lloyd iteration in double until no centroid moves by
+ * 1e-15) rounded to
  * fp32, thresholds = fp32 of the midpoints; Pi = Q diag(sign(diag R)) of the
  * Householder QR of a d x d Gaussian matrix; S = m x d Gaussian.  Gaussians
  * come from SplitMix64 (state = seed) turned into Box-Muller pairs (cos first),
@@ -150,15 +151,17 @@ tq_status tq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_
  *   k, v          host structs holding device pointers; k->t_cap == v->t_cap.
  *   seq_len       device int32[batch]: tokens to attend per sequence; values are
  *                 clamped to [0, t_cap].
- *   n_q_heads     multiple of n_kv_heads; q head h reads kv head h / (H_q/H_kv).
+ *   n_q_heads     n_kv_heads times 1, 2, 4 or 8 (else TQ_ERR_UNSUPPORTED); q head h
+ *                 reads kv head h / (H_q/H_kv).
  *   softmax_scale <= 0 selects 1/sqrt(d).
  *   out           device [batch][n_q_heads][d] of out_dtype; a sequence with
  *                 seq_len 0 gets zeros.  bf16 output is the round-to-nearest-even
  *                 of the fp32 result.
  *   dbg_scores    NULL or device float[batch][n_q_heads][t_cap]: the scaled
  *                 logits l_t for t < seq_len (other entries untouched).
- *   workspace     device buffer of at least tq_decode_workspace_bytes bytes,
- *                 256-byte aligned; its contents on entry do not matter.
+ *   workspace     device scratch of at least tq_decode_workspace_bytes bytes,
+ *                 256-byte aligned; its contents on entry do not matter.  Calls
+ *                 that share a workspace must not overlap in time.
  * Score: l_t = scale * nu_t * ( <Pi q, c_k[code_t]> + sqrt(pi/2)/m * gamma_t *
  * <S Pi q, 2 z_t - 1> ); output o = Pi_v^T sum_t softmax(l)_t nu^v_t c_v[code^v_t].
  * Deterministic: the same inputs give bitwise-identical outputs. */

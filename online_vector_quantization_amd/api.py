@@ -227,6 +227,7 @@ def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, t_cap: i
 
 
 def alloc_workspace(batch: int, n_q_heads: int, n_kv_heads: int, t_cap: int, device) -> torch.Tensor:
+    """Device scratch for tq_decode_attention."""
     n = decode_workspace_bytes(batch, n_q_heads, n_kv_heads, t_cap)
     return torch.empty(n, dtype=torch.uint8, device=device)
 

@@ -89,6 +89,10 @@ tq_status upload_tables(tq_codebook *cb) {
   off = align256(off + static_cast<size_t>(m) * d * sizeof(float));
   cb->off_qjl_t_f32 = off;
   off = align256(off + static_cast<size_t>(m) * d * sizeof(float));
+  cb->off_key_lut = off;
+  off = align256(off + tq::kKeyLutBytes);
+  cb->off_pair_lut = off;
+  off = align256(off + tq::kPairLutBytes);
   cb->dev_bytes = off;
 
   std::vector<unsigned char> img(off, 0);
@@ -105,6 +109,18 @@ tq_status upload_tables(tq_codebook *cb) {
     float *st = reinterpret_cast<float *>(img.data() + cb->off_qjl_t_f32);
     for (int i = 0; i < d; ++i)
       for (int r = 0; r < m; ++r) st[i * m + r] = h.qjl[static_cast<size_t>(r) * d + i];
+  }
+  {
+    const int b = h.bits, mask = (1 << b) - 1;
+    const int entries = 1 << tq::key_lut_bits(b), coords = tq::key_lut_coords(b);
+    float *kl = reinterpret_cast<float *>(img.data() + cb->off_key_lut);
+    for (int e = 0; e < entries; ++e)
+      for (int c = 0; c < coords; ++c) kl[e * coords + c] = h.centroids[(e >> (c * b)) & mask];
+    float *pl = reinterpret_cast<float *>(img.data() + cb->off_pair_lut);
+    for (int e = 0; e < (1 << (2 * b)); ++e) {
+      pl[2 * e] = h.centroids[e & mask];
+      pl[2 * e + 1] = h.centroids[(e >> b) & mask];
+    }
   }
   DeviceGuard guard(cb->device);
   if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice(%d): %s", cb->device, hipGetErrorString(guard.err));
@@ -270,6 +286,7 @@ tq_status tq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || t_cap < 1 || n_q_heads % n_kv_heads != 0)
     return fail(TQ_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d/%d, t_cap %lld)", batch, n_q_heads, n_kv_heads,
                 static_cast<long long>(t_cap));
+
   *bytes = tq::plan_decode(batch, n_q_heads, n_kv_heads, t_cap).total_bytes;
   return ok();
 }
@@ -291,10 +308,11 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0)
     return fail(TQ_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d/%d)", batch, n_q_heads, n_kv_heads);
   const int g = n_q_heads / n_kv_heads;
-  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
-    return fail(TQ_ERR_UNSUPPORTED, "q heads per kv head must be 1, 2, 4, 8 or 16 (got %d)", g);
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(TQ_ERR_UNSUPPORTED, "q heads per kv head must be 1, 2, 4 or 8 (got %d)", g);
   if (k->t_cap < 1 || v->t_cap != k->t_cap) return fail(TQ_ERR_INVALID_ARG, "key/value t_cap must match and be >= 1");
   if (k->t_cap > (int64_t{1} << 30)) return fail(TQ_ERR_UNSUPPORTED, "t_cap above 2^30");
+
   const int m = kcb->host.m;
   if (k->codes == nullptr || k->norms == nullptr || v->codes == nullptr || v->norms == nullptr)
     return fail(TQ_ERR_INVALID_ARG, "cache codes/norms are required");
@@ -332,12 +350,10 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
   a.rot_k_t = dev_ptr<float>(kcb, kcb->off_rot_t_f32);
   a.qjl_t = m > 0 ? dev_ptr<float>(kcb, kcb->off_qjl_t_f32) : nullptr;
   a.rot_v = dev_ptr<float>(vcb, vcb->off_rot_f32);
-  for (int i = 0; i < tq::kMaxLevels; ++i) {
-    a.k_centroids[i] = i < kcb->host.levels ? kcb->host.centroids[i] : 0.f;
-    a.v_centroids[i] = i < vcb->host.levels ? vcb->host.centroids[i] : 0.f;
-  }
+  a.k_lut = dev_ptr<float>(kcb, kcb->off_key_lut);
+  a.v_lut = dev_ptr<float>(vcb, vcb->off_pair_lut);
   unsigned char *ws = static_cast<unsigned char *>(workspace);
-  a.ws_qprep = reinterpret_cast<float *>(ws + plan.off_qprep);
+  a.ws_qslot = reinterpret_cast<float *>(ws + plan.off_qslot);
   a.ws_part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
   a.ws_part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
   a.chunk = plan.chunk;

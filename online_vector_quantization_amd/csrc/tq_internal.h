@@ -51,4 +51,6 @@ struct tq_codebook {
   size_t off_rot_t_f32 = 0;       // float[d*d] row-major Pi^T
   size_t off_qjl_f32 = 0;         // float[m*d] row-major S
   size_t off_qjl_t_f32 = 0;       // float[d*m] row-major S^T
+  size_t off_key_lut = 0;         // decode key dequantization table
+  size_t off_pair_lut = 0;        // decode value pair table
 };

@@ -44,12 +44,25 @@ void pack_encode_fragments(const float *mat, void *dst);
 hipError_t launch_encode(const EncodeArgs &a, int bits, bool qjl, bool x_f32, int num_cus,
                          hipStream_t stream);
 
+constexpr int kMaxDecodeChunks = 128;   // chunks per (batch, kv head)
+
+// Decode dequantization tables (built once per codebook on the host).
+// Key table: one lookup turns kCoords codes into floats:
+//   b'=1: 4 bits (4 codes), 16 entries;  b'=2: 8 bits (4 codes), 256 entries;
+//   b'=3: 6 bits (2 codes), 64 entries;  b'=4: 8 bits (2 codes), 256 entries.
+// Entry e, coordinate c holds centroid[(e >> (c * b')) & (2^b' - 1)].
+constexpr int key_lut_bits(int b) { return b == 1 ? 4 : (b == 3 ? 6 : 8); }
+constexpr int key_lut_coords(int b) { return key_lut_bits(b) / b; }
+constexpr size_t kKeyLutBytes = 256 * 4 * sizeof(float);     // largest key table
+// Value pair table: 2^(2b) entries of (centroid[e & m], centroid[(e >> b) & m]).
+constexpr size_t kPairLutBytes = 256 * 2 * sizeof(float);
+
 struct DecodePlan {
   int chunk;               // tokens per work-group chunk
   int n_chunks;
-  size_t off_qprep;        // bytes into the workspace
-  size_t off_part_o;
-  size_t off_part_ml;
+  size_t off_qslot;        // bytes into the workspace: float[groups][g][d + 128], q~ and s per work-group
+  size_t off_part_o;       // float[groups][g][d]: rotated partial outputs
+  size_t off_part_ml;      // float[groups][g][2]: running max and sum
   size_t total_bytes;
 };
 
@@ -76,11 +89,11 @@ struct DecodeArgs {
   const float *rot_k_t;    // Pi_k^T row-major (d x d): entry [i][j] = Pi_k[j][i]
   const float *qjl_t;      // S^T row-major (d x m)
   const float *rot_v;      // Pi_v row-major (d x d)
-  float k_centroids[kMaxLevels];
-  float v_centroids[kMaxLevels];
-  float *ws_qprep;         // [B*Hq][d + m]
-  float *ws_part_o;        // [B*Hq][n_chunks][d]
-  float *ws_part_ml;       // [B*Hq][n_chunks][2]
+  const float *k_lut;      // key dequantization table (kKeyLutBytes)
+  const float *v_lut;      // value pair table (kPairLutBytes)
+  float *ws_qslot;
+  float *ws_part_o;        // [B*Hkv][n_chunks][g][d]
+  float *ws_part_ml;       // [B*Hkv][n_chunks][g][2]
   int chunk, n_chunks;
 };
 
