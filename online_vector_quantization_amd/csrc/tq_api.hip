@@ -93,6 +93,8 @@ tq_status upload_tables(tq_codebook *cb) {
   off = align256(off + tq::kKeyLutBytes);
   cb->off_pair_lut = off;
   off = align256(off + tq::kPairLutBytes);
+  cb->off_qcells = off;
+  off = align256(off + tq::kQuantCells * 4 * sizeof(float));
   cb->dev_bytes = off;
 
   std::vector<unsigned char> img(off, 0);
@@ -122,6 +124,9 @@ tq_status upload_tables(tq_codebook *cb) {
       pl[2 * e + 1] = h.centroids[(e >> b) & mask];
     }
   }
+  if (!tq::build_quant_cells(h.thresholds.data(), h.centroids.data(), h.levels,
+                             reinterpret_cast<float *>(img.data() + cb->off_qcells), &cb->qscale, &cb->qbias))
+    return fail(TQ_ERR_UNSUPPORTED, "codebook thresholds do not fit the quantizer cell grid");
   DeviceGuard guard(cb->device);
   if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice(%d): %s", cb->device, hipGetErrorString(guard.err));
   hipError_t e = hipMalloc(&cb->dev_buf, off);
@@ -268,10 +273,9 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *x, tq_dtype x_dtype, i
   a.dbg_proj = dbg_proj;
   a.frag_rot = dev_ptr<uint4>(cb, cb->off_rot_frag);
   a.frag_qjl = (m > 0) ? dev_ptr<uint4>(cb, cb->off_qjl_frag) : nullptr;
-  for (int i = 0; i < tq::kMaxLevels; ++i) {
-    a.centroids[i] = i < cb->host.levels ? cb->host.centroids[i] : 0.f;
-    a.thresholds[i] = i < cb->host.levels - 1 ? cb->host.thresholds[i] : INFINITY;
-  }
+  a.qlut = dev_ptr<float4>(cb, cb->off_qcells);
+  a.qscale = cb->qscale;
+  a.qbias = cb->qbias;
   DeviceGuard guard(cb->device);
   if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
   hipError_t e = tq::launch_encode(a, cb->host.bits, m > 0, x_dtype == TQ_F32, cu_count(cb->device),

@@ -7,7 +7,7 @@
 // [intelliparadigm "3-bit" article, §2.1.2]: keys also store sign(S r) of the
 // residual r, binarized as `projected > 0`.
 //
-// Design (one wave = 16*NT vectors per tile):
+// Design (one wave = 16*NT vectors per tile, 8 waves per work-group):
 //  * Both products are dense 128x128 contractions, so they run on MFMA
 //    (v_mfma_f32_16x16x32_bf16, fp32 accumulate).  To keep fp32-level
 //    accuracy the fp32 matrices are split into bf16 hi + lo parts: bf16 inputs
@@ -20,11 +20,17 @@
 //    accumulators.  Every later step (quantize, residual, second GEMM's B
 //    operand, sign word, code words) then stays inside the lane: no shuffles
 //    except the two xor-reductions for the norms.
+//  * Quantization is exact threshold counting through a fine cell table: the
+//    cell of y gives the number of thresholds surely below y and the one
+//    threshold (if any) that can still lie between, plus the two centroids
+//    the residual needs; one comparison finishes the count.
 //  * Pi and S fragments (32 KiB per bf16 split) are staged once per
-//    work-group in LDS; work-groups are persistent and grid-stride over tiles.
+//    work-group in LDS; work-groups are persistent and grid-stride over
+//    tiles; two waves per SIMD overlap one wave's loads with the other's math.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 
 #include "tq_internal.h"
@@ -37,7 +43,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFragU4 = static_cast<int>(kFragBytesPerSplit / 16);  // uint4 per split
 
@@ -57,18 +63,40 @@ __device__ __forceinline__ void split_bf16(const f32x8 &v, bf16x8 &hi, bf16x8 &l
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// One lane's 32 input coordinates of one vector.
+template <bool XF32> struct XRegs;
+template <> struct XRegs<false> { uint4 w[4]; };
+template <> struct XRegs<true> { float4 w[8]; };
+
+template <bool XF32, int NT>
+__device__ __forceinline__ void load_x(const EncodeArgs &a, int64_t tile, int j, int kk, XRegs<XF32> (&x)[NT]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t vec = tile * (16 * NT) + nt * 16 + j;
+    const bool valid = vec < a.n;
+    if constexpr (!XF32) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + vec * a.x_stride + 32 * kk);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) x[nt].w[s] = valid ? src[s] : make_uint4(0, 0, 0, 0);
+    } else {
+      const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + vec * a.x_stride + 32 * kk);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) x[nt].w[s] = valid ? src[s] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
 template <int BITS, bool QJL, bool XF32, int NT>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
-  constexpr int L = 1 << BITS;
   __shared__ uint4 s_frag[(QJL ? 4 : 2) * kFragU4];
-  __shared__ float s_cent[kMaxLevels];
+  __shared__ float4 s_qlut[kQuantCells];
 
   const int tid = threadIdx.x;
   for (int i = tid; i < 2 * kFragU4; i += kThreads) s_frag[i] = a.frag_rot[i];
   if constexpr (QJL) {
     for (int i = tid; i < 2 * kFragU4; i += kThreads) s_frag[2 * kFragU4 + i] = a.frag_qjl[i];
   }
-  if (tid < kMaxLevels) s_cent[tid] = a.centroids[tid];
+  for (int i = tid; i < kQuantCells; i += kThreads) s_qlut[i] = a.qlut[i];
   __syncthreads();
 
   const uint4 *rot_hi = s_frag;
@@ -82,27 +110,29 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   const int kk = lane >> 4;
   const int64_t n = a.n;
   const int64_t tiles = (n + 16 * NT - 1) / (16 * NT);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  const float qscale = a.qscale, qbias = a.qbias;
 
-  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + wave; tile < tiles;
-       tile += static_cast<int64_t>(gridDim.x) * kWaves) {
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + wave; tile < tiles; tile += stride) {
+    XRegs<XF32> cur[NT];
+    load_x<XF32, NT>(a, tile, j, kk, cur);
+
     int64_t vec[NT];
     bool valid[NT];
     bf16x8 bx[NT][4];
     bf16x8 bxlo[NT][4];
     float nu[NT], inv[NT];
 
-    // ---- load 32 consecutive coordinates of one vector per lane; norms
+    // ---- B operands and norms
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       vec[nt] = tile * (16 * NT) + nt * 16 + j;
       valid[nt] = vec[nt] < n;
       float ss = 0.f;
       if constexpr (!XF32) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            static_cast<const uint16_t *>(a.x) + vec[nt] * a.x_stride + 32 * kk);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          uint4 w = valid[nt] ? src[s] : make_uint4(0, 0, 0, 0);
+          const uint4 w = cur[nt].w[s];
           bx[nt][s] = u4_as_bf16(w);
           const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -114,12 +144,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
           }
         }
       } else {
-        const float4 *src = reinterpret_cast<const float4 *>(
-            static_cast<const float *>(a.x) + vec[nt] * a.x_stride + 32 * kk);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          float4 p0 = valid[nt] ? src[2 * s] : make_float4(0.f, 0.f, 0.f, 0.f);
-          float4 p1 = valid[nt] ? src[2 * s + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float4 p0 = cur[nt].w[2 * s], p1 = cur[nt].w[2 * s + 1];
           const f32x8 v = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
@@ -132,7 +159,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
       inv[nt] = (nu[nt] == 0.f) ? 0.f : 1.f / nu[nt];
     }
 
-    // ---- y = Pi x (M = output coordinate, N = vector, K = input coordinate)
+    // ---- y = Pi x (M = output coordinate, N = vector, K = input coordinate);
+    // consecutive MFMAs always target different accumulators.
     f32x4 acc[NT][8];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -140,54 +168,76 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
       for (int t = 0; t < 8; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      // keep the scheduler from hoisting every fragment load of the tile
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const bf16x8 ah = u4_as_bf16(rot_hi[(t * 4 + s) * 64 + lane]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][t] = mfma(ah, bx[nt][s], acc[nt][t]);
+        if constexpr (XF32) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt][t] = mfma(ah, bxlo[nt][s], acc[nt][t]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
         const bf16x8 al = u4_as_bf16(rot_lo[(t * 4 + s) * 64 + lane]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          acc[nt][t] = mfma(ah, bx[nt][s], acc[nt][t]);
-          acc[nt][t] = mfma(al, bx[nt][s], acc[nt][t]);
-          if constexpr (XF32) acc[nt][t] = mfma(ah, bxlo[nt][s], acc[nt][t]);
-        }
+        for (int nt = 0; nt < NT; ++nt) acc[nt][t] = mfma(al, bx[nt][s], acc[nt][t]);
       }
     }
 
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- quantize, residual, pack (lane holds y[32kk + 4t + e] of vector vec[nt])
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      // lane holds y[32kk + 4t + e] of vector vec[nt] in acc[nt][t][e]
       uint32_t words[BITS];
 #pragma unroll
       for (int w = 0; w < BITS; ++w) words[w] = 0u;
       float rr = 0.f;
+      const bool dbg = a.dbg_rot != nullptr && valid[nt];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
+        float yv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float y = acc[nt][t][e] * inv[nt];
-          uint32_t idx = 0;
-#pragma unroll
-          for (int i = 0; i < L - 1; ++i) idx += (y >= a.thresholds[i]) ? 1u : 0u;
+          yv[e] = y;
+          // cell of y: thresholds below the cell are counted in q.x; q.y is the
+          // only threshold that may lie in the cell (NaN when none); q.z / q.w
+          // are the centroids below / above it.
+          const int cell = min(max(static_cast<int>(fmaf(y, qscale, qbias)), 0), kQuantCells - 1);
+          const float4 q = s_qlut[cell];
+          const bool up = y >= q.y;
+          const uint32_t idx = __float_as_uint(q.x) + (up ? 1u : 0u);
           const int pos = (4 * t + e) * BITS;
           words[pos / 32] |= idx << (pos % 32);
           if ((pos % 32) + BITS > 32) words[pos / 32 + 1] |= idx >> (32 - (pos % 32));
           if constexpr (QJL) {
-            const float r = y - s_cent[idx];
+            const float r = y - (up ? q.w : q.z);
             rr = fmaf(r, r, rr);
             acc[nt][t][e] = r;   // keep the residual in place of y
-          } else {
-            acc[nt][t][e] = y;
           }
-          if (a.dbg_rot != nullptr && valid[nt]) a.dbg_rot[vec[nt] * kHeadDim + 32 * kk + 4 * t + e] = y;
         }
+        if (dbg)
+          *reinterpret_cast<float4 *>(a.dbg_rot + vec[nt] * kHeadDim + 32 * kk + 4 * t) =
+              make_float4(yv[0], yv[1], yv[2], yv[3]);
       }
       int64_t row = vec[nt];
       if (a.dst_row != nullptr) row = valid[nt] ? a.dst_row[vec[nt]] : -1;
       const bool ok = valid[nt] && row >= 0 && row < a.cache_rows;
       if (ok) {
         uint32_t *cp = a.codes + row * (4 * BITS) + kk * BITS;
+        if constexpr (BITS == 4) {
+          *reinterpret_cast<uint4 *>(cp) = make_uint4(words[0], words[1], words[2], words[3]);
+        } else if constexpr (BITS == 2) {
+          *reinterpret_cast<uint2 *>(cp) = make_uint2(words[0], words[1]);
+        } else {
 #pragma unroll
-        for (int w = 0; w < BITS; ++w) cp[w] = words[w];
+          for (int w = 0; w < BITS; ++w) cp[w] = words[w];
+        }
       }
       if constexpr (QJL) {
         rr += __shfl_xor(rr, 16);
@@ -199,16 +249,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
 
     if constexpr (QJL) {
       // ---- p = S r (M = projection index, N = vector, K = rotated coordinate)
-      bf16x8 rh[NT][4], rl[NT][4];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const f32x8 v = {acc[nt][2 * s][0],     acc[nt][2 * s][1],     acc[nt][2 * s][2],
-                           acc[nt][2 * s][3],     acc[nt][2 * s + 1][0], acc[nt][2 * s + 1][1],
-                           acc[nt][2 * s + 1][2], acc[nt][2 * s + 1][3]};
-          split_bf16(v, rh[nt][s], rl[nt][s]);
-        }
       f32x4 accp[NT][8];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -216,30 +256,45 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
         for (int t = 0; t < 8; ++t) accp[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 rh[NT], rl[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const f32x8 v = {acc[nt][2 * s][0],     acc[nt][2 * s][1],     acc[nt][2 * s][2],
+                           acc[nt][2 * s][3],     acc[nt][2 * s + 1][0], acc[nt][2 * s + 1][1],
+                           acc[nt][2 * s + 1][2], acc[nt][2 * s + 1][3]};
+          split_bf16(v, rh[nt], rl[nt]);
+        }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const bf16x8 ah = u4_as_bf16(qjl_hi[(t * 4 + s) * 64 + lane]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) accp[nt][t] = mfma(ah, rh[nt], accp[nt][t]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) accp[nt][t] = mfma(ah, rl[nt], accp[nt][t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
           const bf16x8 al = u4_as_bf16(qjl_lo[(t * 4 + s) * 64 + lane]);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            accp[nt][t] = mfma(ah, rh[nt][s], accp[nt][t]);
-            accp[nt][t] = mfma(al, rh[nt][s], accp[nt][t]);
-            accp[nt][t] = mfma(ah, rl[nt][s], accp[nt][t]);
-          }
+          for (int nt = 0; nt < NT; ++nt) accp[nt][t] = mfma(al, rh[nt], accp[nt][t]);
         }
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
+        // sign word: bit (4t + e) = [p > 0]; built most significant bit first
         uint32_t sw = 0u;
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int t = 7; t >= 0; --t)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p = accp[nt][t][e];
-            sw |= (p > 0.f ? 1u : 0u) << (4 * t + e);
-            if (a.dbg_proj != nullptr && valid[nt])
-              a.dbg_proj[vec[nt] * kQjlDim + 32 * kk + 4 * t + e] = p;
-          }
+          for (int e = 3; e >= 0; --e) sw = (sw << 1) | (accp[nt][t][e] > 0.f ? 1u : 0u);
+        if (a.dbg_proj != nullptr && valid[nt]) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            *reinterpret_cast<float4 *>(a.dbg_proj + vec[nt] * kQjlDim + 32 * kk + 4 * t) =
+                make_float4(accp[nt][t][0], accp[nt][t][1], accp[nt][t][2], accp[nt][t][3]);
+        }
         int64_t row = vec[nt];
         if (a.dst_row != nullptr) row = valid[nt] ? a.dst_row[vec[nt]] : -1;
         if (valid[nt] && row >= 0 && row < a.cache_rows) a.signs[row * (kQjlDim / 32) + kk] = sw;
@@ -253,8 +308,7 @@ hipError_t launch_t(const EncodeArgs &a, int num_cus, hipStream_t stream) {
   constexpr int NT = 2;
   const int64_t tiles = (a.n + 16 * NT - 1) / (16 * NT);
   const int64_t wgs = (tiles + kWaves - 1) / kWaves;
-  const int per_cu = QJL ? 1 : 2;
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(wgs, static_cast<int64_t>(num_cus) * per_cu)));
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(wgs, num_cus)));
   hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, NT>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -285,6 +339,40 @@ void pack_encode_fragments(const float *mat, void *dst) {
             const uint16_t val = split == 0 ? hi : bf16_bits_rne(v - bf16_bits_to_float(hi));
             out[((((split * 8 + t) * 4 + s) * 64 + lane) * 8) + e] = val;
           }
+}
+
+bool build_quant_cells(const float *thresholds, const float *centroids, int levels, float *cells,
+                       float *qscale, float *qbias) {
+  // Cells of width w over [-Y, Y) with Y = 0.5; the kernel computes
+  // cell = clamp(int(y * K/(2Y) + K/2), 0, K-1).  For each cell: the count of
+  // thresholds below (lo - eps), the single threshold in [lo - eps, hi + eps]
+  // (NaN if none) and the centroids on either side of it.  eps covers the
+  // rounding of the cell computation; more than one candidate fails the build.
+  const double Y = 0.5, w = 2.0 * Y / kQuantCells, eps = 0.05 * w;
+  const int nt = levels - 1;
+  for (int i = 0; i < nt; ++i)
+    if (!(std::fabs(thresholds[i]) < Y - 2 * w)) return false;
+  for (int k = 0; k < kQuantCells; ++k) {
+    const double lo = -Y + k * w, hi = lo + w;
+    int below = 0, cand = -1, ncand = 0;
+    for (int i = 0; i < nt; ++i) {
+      if (thresholds[i] < lo - eps) {
+        ++below;
+      } else if (thresholds[i] <= hi + eps) {
+        ++ncand;
+        cand = i;
+      }
+    }
+    if (ncand > 1 || (ncand == 1 && cand != below)) return false;
+    uint32_t cbits = static_cast<uint32_t>(below);
+    std::memcpy(&cells[4 * k], &cbits, 4);
+    cells[4 * k + 1] = ncand ? thresholds[cand] : std::nanf("");
+    cells[4 * k + 2] = centroids[below];
+    cells[4 * k + 3] = centroids[std::min(below + 1, levels - 1)];
+  }
+  *qscale = static_cast<float>(kQuantCells / (2.0 * Y));
+  *qbias = static_cast<float>(kQuantCells / 2.0);
+  return true;
 }
 
 hipError_t launch_encode(const EncodeArgs &a, int bits, bool qjl, bool x_f32, int num_cus,

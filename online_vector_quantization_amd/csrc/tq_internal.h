@@ -53,4 +53,6 @@ struct tq_codebook {
   size_t off_qjl_t_f32 = 0;       // float[d*m] row-major S^T
   size_t off_key_lut = 0;         // decode key dequantization table
   size_t off_pair_lut = 0;        // decode value pair table
+  size_t off_qcells = 0;          // encode quantizer cell table
+  float qscale = 0.f, qbias = 0.f;
 };

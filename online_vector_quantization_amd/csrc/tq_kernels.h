@@ -18,6 +18,9 @@ constexpr int kMaxLevels = 16;   // 2^4
 constexpr size_t kFragBytesPerSplit = 8 * 4 * 64 * 16;   // 32 KiB
 constexpr size_t kFragBytes = 2 * kFragBytesPerSplit;     // hi + lo
 
+// Quantizer cell table: kQuantCells float4 entries (see build_quant_cells).
+constexpr int kQuantCells = 512;
+
 struct EncodeArgs {
   const void *x;
   int64_t x_stride;        // elements between rows
@@ -32,13 +35,18 @@ struct EncodeArgs {
   float *dbg_proj;
   const uint4 *frag_rot;   // kFragBytes
   const uint4 *frag_qjl;   // kFragBytes (keys with QJL)
-  float centroids[kMaxLevels];
-  float thresholds[kMaxLevels];
+  const float4 *qlut;      // kQuantCells quantizer cells
+  float qscale, qbias;     // cell = clamp(int(y * qscale + qbias), 0, kQuantCells - 1)
 };
 
 // Fills `dst` (kFragBytes) with the hi/lo bf16 fragments of the 128 x 128
 // row-major matrix `mat` (rows = outputs, columns = inputs).
 void pack_encode_fragments(const float *mat, void *dst);
+
+// Builds the quantizer cell table (4 floats per cell); false if the
+// thresholds do not fit the cell grid (then the GPU path is unsupported).
+bool build_quant_cells(const float *thresholds, const float *centroids, int levels, float *cells,
+                       float *qscale, float *qbias);
 
 // Enqueues the encode kernel; returns the launch error (hipSuccess on success).
 hipError_t launch_encode(const EncodeArgs &a, int bits, bool qjl, bool x_f32, int num_cus,
