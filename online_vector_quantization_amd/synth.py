@@ -135,3 +135,28 @@ def bulk(n: int, config_id: int = 4):
     v = bf16_bits(kv_block(sv, 1, 1, n, student_t_rate=0.01)[0, 0])
     q = bf16_bits(sq.standard_normal((1, 64, D), dtype=np.float32))
     return k, v, q
+
+
+def bulk_device(n: int, device, config_id: int = 4, chunk: int = 1 << 22):
+    """Bulk-encode inputs generated on the GPU (seeded torch generator):
+    K and V [n, D] bf16, N(0,1) with 1% of tokens redrawn iid Student-t(3)
+    (a normal over the square root of a chi-square(3)/3 draw), and 64 N(0,1)
+    queries.  Used where a host generator would take minutes."""
+    import torch
+    g = torch.Generator(device=device)
+    out = []
+    for which in range(2):
+        g.manual_seed(int(np.random.SeedSequence([config_id, which]).generate_state(1)[0]))
+        x = torch.empty(n, D, dtype=torch.bfloat16, device=device)
+        for s in range(0, n, chunk):
+            e = min(n, s + chunk)
+            v = torch.randn(e - s, D, generator=g, device=device)
+            heavy = torch.rand(e - s, generator=g, device=device) < 0.01
+            chi2 = torch.randn(e - s, D, 3, generator=g, device=device).pow(2).sum(-1)
+            t3 = torch.randn(e - s, D, generator=g, device=device) / torch.sqrt(chi2 / 3.0)
+            v = torch.where(heavy[:, None], t3, v)
+            x[s:e] = v.to(torch.bfloat16)
+        out.append(x)
+    g.manual_seed(int(np.random.SeedSequence([config_id, 2]).generate_state(1)[0]))
+    q = torch.randn(1, 64, D, generator=g, device=device).to(torch.bfloat16)
+    return out[0], out[1], q
