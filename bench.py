@@ -31,6 +31,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+
+# HBM bytes per key-encode launch on the 8B layer (262144 vectors), from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this benchmark with
+# --calib-copy 512, each scaled by the ratio of a 512 MiB device copy's known
+# bytes to what the same counter read for it.  Valid only for the encode
+# source they were taken on (sha256 below); otherwise reported as null.
+ENCODE_TRAFFIC = {"source_sha256": "e5948138fecbc9e4cc8b7f0a189e501e944ce3f8ac9bf165e7bb6ccac2fc7489",
+                  "workload": "llama3-8b-layer-b1-s32768",
+                  "fetch_bytes": 68520455, "write_bytes": 14701427}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attn HBM GB/s (% of peak) on compressed KV; encode Mvectors/s"
 
@@ -43,7 +52,11 @@ def parse():
     ap.add_argument("--config", default="llama8b", choices=["llama8b", "llama70b", "batched2", "batched4"])
     ap.add_argument("--hot", action="store_true", help="no replica rotation (cache-resident numbers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 18, help="vectors per tensor in the oracle encode sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle step until this much CPU time has run")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="before warm-up, run 3 plain device copies of MIB MiB (untimed): the reference "
+                         "kernel of known size that scales the HBM byte counters")
     return ap.parse_args()
 
 
@@ -107,6 +120,15 @@ def main():
     def decode(i_c):
         kc, vc = caches[i_c]
         T.decode_attention(kcb, vcb, q, kc, vc, seq, out=out, workspace=ws, stream=stream)
+
+    if args.calib_copy:
+        n_el = args.calib_copy << 18           # MiB of float32
+        src = torch.ones(n_el, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # fill every cache replica once (untimed), then warm up
     for i in range(n_cache):
@@ -181,7 +203,7 @@ def main():
         "roofline": {
             "kernel": "encode (keys: rotation + QJL)", "bound": "hbm",
             "achieved": round(enc_k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4), "traffic": encode_traffic(wl.name),
             "algorithmic_bytes_per_launch": enc_k_bytes, "avg_launch_us": round(float(enc_k.mean()) * 1e3, 2),
             "mfma_tflops_algorithmic": round(enc_k_tflops, 1),
         },
@@ -198,12 +220,28 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, sample):
-    """The CPU oracle (float64 numpy) on a bounded sample of the same workload."""
+def encode_traffic(workload_name):
+    """Counter-measured HBM bytes of one key-encode launch, or None when the
+    figures are missing or the encode source changed since they were taken."""
+    import hashlib
+    src = os.path.join(ROOT, "online_vector_quantization_amd", "csrc", "tq_encode.hip")
+    t = ENCODE_TRAFFIC
+    if t["source_sha256"] is None or workload_name != t["workload"]:
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["source_sha256"]:
+            return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+def cpu_baseline(wl, min_seconds):
+    """The CPU oracle (float64 numpy) on the same step: encode every K and V
+    vector of the layer, then decode all q heads over the full cache.  The step
+    is repeated until at least `min_seconds` of CPU work have run."""
     import oracle as O
     from online_vector_quantization_amd import synth
     try:
@@ -211,37 +249,41 @@ def cpu_baseline(wl, sample):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
+    B, Hkv, S = wl.batch, wl.n_kv_heads, wl.seq_len
     kb = wl.k_bits - 1
     c_k, t_k = O.build_codebook(128, kb)
     c_v, t_v = O.build_codebook(128, wl.v_bits)
     Pi = O.haar_rotation(128, 0)
     Sm = O.qjl_matrix(128, 128, 1)
-    kx = synth.bf16_to_f32(wl.k.reshape(-1, 128)[:sample])
-    vx = synth.bf16_to_f32(wl.v.reshape(-1, 128)[:sample])
-    t0 = time.perf_counter()
-    ek = O.encode(kx, Pi, c_k, t_k, Sm)
-    k_codes = O.pack_bits(ek["idx"], kb)
-    k_signs = O.pack_bits(ek["z"], 1)
-    ev = O.encode(vx, Pi, c_v, t_v)
-    v_codes = O.pack_bits(ev["idx"], wl.v_bits)
-    t_enc = time.perf_counter() - t0
-    # decode over the encoded sample, viewed as one (batch, kv head) row of `sample` tokens
-    kcache = {"codes": k_codes[None, None], "signs": k_signs[None, None], "norms": ek["nu"][None, None],
-              "res_norms": ek["gamma"][None, None]}
-    vcache = {"codes": v_codes[None, None], "norms": ev["nu"][None, None]}
-    g = wl.n_q_heads // wl.n_kv_heads
-    qh = synth.bf16_to_f32(wl.q[0, :g]).astype(np.float64)[None]
-    t1 = time.perf_counter()
-    O.decode_attention(qh, kcache, vcache, [sample], {"bits": kb, "centroids": c_k, "Pi": Pi, "S": Sm},
-                       {"bits": wl.v_bits, "centroids": c_v, "Pi": Pi})
-    t_dec = time.perf_counter() - t1
+    kx = synth.bf16_to_f32(wl.k.reshape(-1, 128))
+    vx = synth.bf16_to_f32(wl.v.reshape(-1, 128))
+    qh = synth.bf16_to_f32(wl.q).astype(np.float64)
+    shape = (B, Hkv, S)
+    t_enc = t_dec = 0.0
+    reps = 0
+    while reps == 0 or t_enc + t_dec < min_seconds:
+        t0 = time.perf_counter()
+        ek = O.encode(kx, Pi, c_k, t_k, Sm)
+        ev = O.encode(vx, Pi, c_v, t_v)
+        kcache = {"codes": O.pack_bits(ek["idx"], kb).reshape(*shape, -1),
+                  "signs": O.pack_bits(ek["z"], 1).reshape(*shape, -1),
+                  "norms": ek["nu"].reshape(shape), "res_norms": ek["gamma"].reshape(shape)}
+        vcache = {"codes": O.pack_bits(ev["idx"], wl.v_bits).reshape(*shape, -1), "norms": ev["nu"].reshape(shape)}
+        t1 = time.perf_counter()
+        O.decode_attention(qh, kcache, vcache, [S] * B, {"bits": kb, "centroids": c_k, "Pi": Pi, "S": Sm},
+                           {"bits": wl.v_bits, "centroids": c_v, "Pi": Pi})
+        t2 = time.perf_counter()
+        t_enc += t1 - t0
+        t_dec += t2 - t1
+        reps += 1
+    n_vec = B * Hkv * S
     rec = (4 * 4 * kb + 16 + 8) + (4 * 4 * wl.v_bits + 4)
-    dec_gbps = sample * rec / t_dec / 1e9
+    dec_gbps = reps * n_vec * rec / t_dec / 1e9
     return {"value": round(dec_gbps, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
-            "encode_mvectors_per_s": round(2 * sample / t_enc / 1e6, 4),
-            "sample": f"first {sample} K and {sample} V vectors of the workload: oracle encode "
-                      f"({t_enc:.2f}s), then oracle decode of {g} q heads over those {sample} tokens "
-                      f"({t_dec:.2f}s); GB/s = compressed bytes read / decode time",
+            "encode_mvectors_per_s": round(reps * 2 * n_vec / t_enc / 1e6, 4),
+            "sample": f"the whole step on the CPU, {reps}x: oracle encode of all {n_vec} K and {n_vec} V vectors "
+                      f"({t_enc / reps:.2f}s each), then oracle decode of all {wl.n_q_heads} q heads over the "
+                      f"{S}-token cache ({t_dec / reps:.2f}s each); GB/s = compressed bytes read / decode time",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
