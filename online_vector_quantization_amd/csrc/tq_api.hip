@@ -85,9 +85,7 @@ tq_status upload_tables(tq_codebook *cb) {
   off = align256(off + static_cast<size_t>(d) * d * sizeof(float));
   cb->off_rot_t_f32 = off;
   off = align256(off + static_cast<size_t>(d) * d * sizeof(float));
-  cb->off_qjl_f32 = off;
-  off = align256(off + static_cast<size_t>(m) * d * sizeof(float));
-  cb->off_qjl_t_f32 = off;
+  cb->off_qjl_rot_t_f32 = off;
   off = align256(off + static_cast<size_t>(m) * d * sizeof(float));
   cb->off_key_lut = off;
   off = align256(off + tq::kKeyLutBytes);
@@ -107,10 +105,16 @@ tq_status upload_tables(tq_codebook *cb) {
   for (int i = 0; i < d; ++i)
     for (int j = 0; j < d; ++j) rt[i * d + j] = h.rotation[static_cast<size_t>(j) * d + i];
   if (m > 0) {
-    std::memcpy(img.data() + cb->off_qjl_f32, h.qjl.data(), h.qjl.size() * sizeof(float));
-    float *st = reinterpret_cast<float *>(img.data() + cb->off_qjl_t_f32);
+    // (S Pi)^T in double, rounded once: the decode projects the raw query
+    // with it (s = S Pi q) instead of projecting Pi q with S.
+    float *st = reinterpret_cast<float *>(img.data() + cb->off_qjl_rot_t_f32);
     for (int i = 0; i < d; ++i)
-      for (int r = 0; r < m; ++r) st[i * m + r] = h.qjl[static_cast<size_t>(r) * d + i];
+      for (int r = 0; r < m; ++r) {
+        double v = 0.0;
+        for (int j = 0; j < d; ++j)
+          v += h.qjl64[static_cast<size_t>(r) * d + j] * h.rotation64[static_cast<size_t>(j) * d + i];
+        st[i * m + r] = static_cast<float>(v);
+      }
   }
   {
     const int b = h.bits, mask = (1 << b) - 1;
@@ -352,7 +356,7 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
   a.out_bf16 = (out_dtype == TQ_BF16);
   a.dbg_scores = dbg_scores;
   a.rot_k_t = dev_ptr<float>(kcb, kcb->off_rot_t_f32);
-  a.qjl_t = m > 0 ? dev_ptr<float>(kcb, kcb->off_qjl_t_f32) : nullptr;
+  a.qjl_rot_t = m > 0 ? dev_ptr<float>(kcb, kcb->off_qjl_rot_t_f32) : nullptr;
   a.rot_v = dev_ptr<float>(vcb, vcb->off_rot_f32);
   a.k_lut = dev_ptr<float>(kcb, kcb->off_key_lut);
   a.v_lut = dev_ptr<float>(vcb, vcb->off_pair_lut);

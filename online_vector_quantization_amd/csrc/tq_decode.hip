@@ -14,19 +14,22 @@
 // streams the packed codes once and keeps everything else on chip.
 //
 // Work-group = (batch b, kv head, chunk of tokens), 8 waves:
-//  0. prologue: q~ = Pi_k q and s = S q~ for the g q heads of this kv head
-//     (parallel partial dot products reduced in LDS); q~, s go to a per-group
-//     workspace slot so that the main loop can read them as scalar (uniform)
-//     operands; a nibble table of signed partial sums of s, a key
-//     dequantization table and a value pair table are built in LDS.
+//  0. prologue: q~ = Pi_k q and s = S q~ = (S Pi_k) q for the g q heads of
+//     this kv head (parallel partial dot products reduced in LDS, all their
+//     global reads issued at once); q~ goes to a per-group workspace slot so
+//     that the main loop can read it as scalar (uniform) operands; a nibble
+//     table of signed partial sums of s, a key dequantization table and a
+//     value pair table are built in LDS.
 //  1. each wave, per 64-token tile:
 //     * scores, one token per lane: key codes dequantized through the LDS
 //       table (one lookup per code byte) times q~ from scalar registers; the
-//       sign term is a sum of nibble-table lookups;
-//     * online softmax (running max and sum per head);
-//     * value sum, two rotated coordinates per lane: the tile's value records
-//       are staged in LDS, each token's weight is broadcast with readlane and a
-//       pair table dequantizes two codes at once.
+//       sign term is a sum of table lookups, each giving 4 signs' partial sum
+//       for all g heads at once;
+//     * online softmax with a lazily raised running max;
+//     * value sum: the tile's weights and value records are staged in LDS
+//       (records read as one coalesced block); lane (token group, coordinate
+//       group) accumulates 8 rotated coordinates x g heads over 16 tokens,
+//       a pair table dequantizing two codes per lookup.
 //  2. the waves merge; the chunk's (max, sum, rotated output) go to the
 //     workspace.
 // A second, small launch merges the chunks of each (b, q head) (log-sum-exp),
@@ -49,9 +52,7 @@ template <int G> struct Geom {
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kParts = kThreads / 128;    // prologue split of the d-long dot products
 };
-constexpr int kSignLut = 32 * 16;       // floats per q head: 32 nibble positions x 16
-constexpr int kRecStride = 20;          // staged value record: up to 16 words, a zero pad word, 16-B rows
-constexpr int kQSlot = D + kQjlDim;     // floats per q head in a workspace slot
+constexpr int kSignLut = 32 * 16;       // sign-table entries per q head: 32 nibble positions x 16
 
 typedef const float __attribute__((address_space(4))) *uniform_fptr;
 
@@ -107,8 +108,8 @@ template <int KW> struct KeyRegs {
   float nu, gamma;
 };
 struct ValRegs {
-  uint4 vc[4];        // value code words (first VW/4 used)
-  float nu_v;
+  uint4 v[4];         // the tile's value code words, read flat: uint4 number lane + 64 k
+  float nu_v;         // this lane's token's value norm
 };
 
 template <int KW, bool QJL>
@@ -127,16 +128,23 @@ __device__ __forceinline__ KeyRegs<KW> load_keys(const DecodeArgs &a, int64_t ro
   return r;
 }
 
-__device__ __forceinline__ ValRegs load_values(const DecodeArgs &a, int64_t row, int VW) {
+// The value records of tokens [tb, tb + n_valid) are consecutive cache rows,
+// so the tile is one contiguous block of 64 * VW words: lane L reads its
+// 16-byte pieces L, L + 64, ... (fully coalesced); pieces of missing tokens
+// read as zero.  The norm is read per token (one per lane).
+__device__ __forceinline__ ValRegs load_values(const DecodeArgs &a, int64_t row_tb, int n_valid, int64_t row_lane,
+                                               int VW, int lane) {
   ValRegs r;
-  const uint4 *vc = reinterpret_cast<const uint4 *>(a.v_codes + row * VW);
+  const uint4 *base = reinterpret_cast<const uint4 *>(a.v_codes + row_tb * VW);
+  const int lim = n_valid * VW;    // words of valid records
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int k = 0; k < 4; ++k) {
+    const int f = lane + 64 * k;
     uint4 t = make_uint4(0, 0, 0, 0);
-    if (w < VW / 4) t = vc[w];
-    r.vc[w] = t;
+    if (4 * k < VW && 4 * f < lim) t = base[f];
+    r.v[k] = t;
   }
-  r.nu_v = a.v_norms[row];
+  r.nu_v = a.v_norms[row_lane];
   return r;
 }
 
@@ -145,15 +153,112 @@ template <int G> struct Lds {
   struct Pro {      // prologue
     float q[G][D];
     float part[GM::kParts][G][D];
-    float qr[G][D];
+    float part_s[GM::kParts][G][D];
     float s[G][D];
+    float qr[G][D];
+  };
+  struct Loop {     // main loop, one region per wave
+    uint32_t vrec[GM::kWaves][64 * 16 + 4];   // a tile's value code words, records back to back (+ pad)
+    float wts[GM::kWaves][64 * G];            // per token, the g heads' weights p * nu_v
   };
   union Shared {
     Pro pro;
-    uint32_t vrec[GM::kWaves][64 * kRecStride];
+    Loop loop;
     float merge[GM::kWaves][G][D];
   };
 };
+
+// g consecutive floats from LDS (one 4-, 8- or 16-byte read per 4 heads)
+template <int G>
+__device__ __forceinline__ void lds_load_g(const float *p, float (&v)[G]) {
+  if constexpr (G == 1) {
+    v[0] = p[0];
+  } else if constexpr (G == 2) {
+    const float2 t = *reinterpret_cast<const float2 *>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+  } else {
+#pragma unroll
+    for (int q4 = 0; q4 < G / 4; ++q4) {
+      const float4 t = reinterpret_cast<const float4 *>(p)[q4];
+      v[4 * q4] = t.x;
+      v[4 * q4 + 1] = t.y;
+      v[4 * q4 + 2] = t.z;
+      v[4 * q4 + 3] = t.w;
+    }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void lds_store_g(float *p, const float (&v)[G]) {
+  if constexpr (G == 1) {
+    p[0] = v[0];
+  } else if constexpr (G == 2) {
+    *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int q4 = 0; q4 < G / 4; ++q4)
+      reinterpret_cast<float4 *>(p)[q4] = make_float4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]);
+  }
+}
+
+// Query-specific lookup tables (sign table, and the key tables below) hold,
+// per nibble position p and nibble value n, one float per head.  Layout: for
+// g <= 4 entry (p, n) is g consecutive floats; for g = 8 the heads are split
+// into two quads, [p][quad][n][4], so that the 64 lanes reading one position
+// (each its own n) touch every LDS bank at most once per 16-byte read.
+template <int G>
+__device__ __forceinline__ int tab_offset(int p, int n, int h) {
+  if constexpr (G <= 4) return (p * 16 + n) * G + h;
+  return ((p * (G / 4) + h / 4) * 16 + n) * 4 + (h & 3);
+}
+
+template <int G>
+__device__ __forceinline__ void tab_load(const float *tab, int p, uint32_t n, float (&v)[G]) {
+  if constexpr (G <= 4) {
+    lds_load_g<G>(tab + (p * 16 + n) * G, v);
+  } else {
+#pragma unroll
+    for (int q4 = 0; q4 < G / 4; ++q4) {
+      const float4 t = reinterpret_cast<const float4 *>(tab + (p * (G / 4) + q4) * 64)[n];
+      v[4 * q4] = t.x;
+      v[4 * q4 + 1] = t.y;
+      v[4 * q4 + 2] = t.z;
+      v[4 * q4 + 3] = t.w;
+    }
+  }
+}
+
+// Entry index e of a table with P positions -> (p, n, h), the inverse of tab_offset.
+template <int G>
+__device__ __forceinline__ void tab_entry(int e, int &p, int &n, int &h) {
+  p = e / (16 * G);
+  const int r = e % (16 * G);
+  if constexpr (G <= 4) {
+    n = r / G;
+    h = r % G;
+  } else {
+    n = (r % 64) / 4;
+    h = (r / 64) * 4 + (r & 3);
+  }
+}
+
+// Key scores by table (for 1- and 2-bit key codes and g >= 2): a nibble of
+// codes covers 4 / b' coordinates, and the table entry (p, n, h) is the
+// partial dot product of q~_h with the centroids that nibble n encodes at
+// position p.  One lookup then replaces 4 / b' multiply-adds per head.
+template <int KB, int G> struct KeyTab {
+  static constexpr bool kOn = (KB == 1 || KB == 2) && G >= 2;
+  static constexpr int kCpn = kOn ? 4 / KB : 1;         // coordinates per nibble
+  static constexpr int kPos = D / kCpn;                  // nibble positions
+  static constexpr int kFloats = kOn ? kPos * 16 * G : 1;
+};
+
+// Softmax weights are exp(l - m) against a running max m that is only raised
+// when a score exceeds it by more than kLazy (then the sums and accumulators
+// are rescaled); otherwise every weight is at most e^kLazy.  The result is the
+// same softmax, with far fewer wave reductions and rescales.
+constexpr float kLazy = 8.f;
 
 template <int KB, bool QJL, int G>
 __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a) {
@@ -166,7 +271,11 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   constexpr int KW = D * KB / 32;   // key code words per token
   __shared__ float s_kdeq[KL::kEntries * KL::kCoords];
   __shared__ float2 s_vdeq[256];
-  __shared__ float s_slut[QJL ? G : 1][kSignLut];
+  // QJL sign table, entry (pos, nib, h) = sum_{k<4} s_h[4 pos + k] * (bit k of nib ? +1 : -1)
+  __shared__ float s_slut[QJL ? kSignLut * G : 1];
+  using KT = KeyTab<KB, G>;
+  constexpr int kFlight = G >= 8 ? 4 : 8;   // table positions read ahead (32 floats for g = 4, 8)
+  __shared__ float s_ktab[KT::kFloats];
   __shared__ typename Lds<G>::Shared sh;
   __shared__ float s_ml[kWaves][G][2];
 
@@ -188,17 +297,21 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   const int t_end = min(T, t_begin + a.chunk);
   const int64_t row0 = static_cast<int64_t>(row_id) * a.t_cap;
   auto row_of = [&](int tb) -> int64_t { return row0 + ((tb + lane < t_end) ? tb + lane : tb); };
-  // First tile's records are requested before the prologue so that their
-  // latency overlaps it.
   const int tb0 = t_begin + wave * 64;
-  KeyRegs<KW> cur{};
-  ValRegs vcur{};
-  if (tb0 < t_end) {
-    cur = load_keys<KW, QJL>(a, row_of(tb0));
-    vcur = load_values(a, row_of(tb0), VW);
-  }
 
   // ------------------------------------------------------------ 0. prologue
+  // Every global read of the prologue is issued up front: this thread's slices
+  // of Pi_k^T and (S Pi_k)^T, the query and the codebook tables.  Thread
+  // (i, part) then forms the partial dot products over j in [kJ part, kJ part + kJ)
+  // of q~_i = sum_j Pi[i][j] q_j and s_i = sum_j (S Pi)[i][j] q_j.
+  const int pi_ = tid & (D - 1), part = tid >> 7;
+  float pv[kJ], sv[QJL ? kJ : 1];
+#pragma unroll
+  for (int jj = 0; jj < kJ; ++jj) pv[jj] = a.rot_k_t[(kJ * part + jj) * D + pi_];
+  if constexpr (QJL) {
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj) sv[jj] = a.qjl_rot_t[(kJ * part + jj) * kQjlDim + pi_];
+  }
   for (int e = tid; e < G * D; e += kThreads)
     sh.pro.q[e / D][e % D] = load_q(a.q, a.q_bf16, static_cast<int64_t>(b * a.n_q_heads + hq0) * D + e);
   {
@@ -211,64 +324,73 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
     for (int e = tid; e < (1 << (2 * VB)) / 2; e += kThreads) vd[e] = vl[e];
   }
   __syncthreads();
-  float *slot = a.ws_qslot + static_cast<int64_t>(group_id) * G * kQSlot;
+  // The first tile's records are requested now: after the prologue's own reads
+  // (the wait for those must not include HBM latency, since memory reads
+  // retire in order) and early enough to overlap the rest of the prologue.
+  KeyRegs<KW> cur{};
+  ValRegs vcur{};
+  if (tb0 < t_end) {
+    cur = load_keys<KW, QJL>(a, row_of(tb0));
+    vcur = load_values(a, row0 + tb0, t_end - tb0, row_of(tb0), VW, lane);
+  }
   {
-    // q~_i = sum_j Pi[i][j] q_j: thread (i, part) sums j in [kJ part, kJ part + kJ)
-    const int i = tid & (D - 1), part = tid >> 7;
-    float acc[G];
+    float aq[G], as[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.f;
-    float pv[kJ];
-#pragma unroll
-    for (int jj = 0; jj < kJ; ++jj) pv[jj] = a.rot_k_t[(kJ * part + jj) * D + i];
+    for (int h = 0; h < G; ++h) {
+      aq[h] = 0.f;
+      as[h] = 0.f;
+    }
 #pragma unroll
     for (int jj = 0; jj < kJ; ++jj)
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = fmaf(pv[jj], sh.pro.q[h][kJ * part + jj], acc[h]);
+      for (int h = 0; h < G; ++h) {
+        const float qj = sh.pro.q[h][kJ * part + jj];
+        aq[h] = fmaf(pv[jj], qj, aq[h]);
+        if constexpr (QJL) as[h] = fmaf(sv[jj], qj, as[h]);
+      }
 #pragma unroll
-    for (int h = 0; h < G; ++h) sh.pro.part[part][h][i] = acc[h];
+    for (int h = 0; h < G; ++h) {
+      sh.pro.part[part][h][pi_] = aq[h];
+      if constexpr (QJL) sh.pro.part_s[part][h][pi_] = as[h];
+    }
   }
   __syncthreads();
+  // q~ goes to this work-group's slot, coordinate-major ([i][h]) so that the
+  // main loop reads a few coordinates of all g heads with one scalar load.
+  float *slot = a.ws_qslot + static_cast<int64_t>(group_id) * G * D;
   for (int e = tid; e < G * D; e += kThreads) {
     const int h = e / D, i = e % D;
-    float v = 0.f;
+    float v = 0.f, w = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < kParts; ++pp) v += sh.pro.part[pp][h][i];
-    sh.pro.qr[h][i] = v;
-    slot[h * kQSlot + i] = v;
-  }
-  if constexpr (QJL) {
-    __syncthreads();
-    const int r = tid & (D - 1), part = tid >> 7;
-    float acc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.f;
-    float sv[kJ];
-#pragma unroll
-    for (int jj = 0; jj < kJ; ++jj) sv[jj] = a.qjl_t[(kJ * part + jj) * kQjlDim + r];
-#pragma unroll
-    for (int jj = 0; jj < kJ; ++jj)
-#pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = fmaf(sv[jj], sh.pro.qr[h][kJ * part + jj], acc[h]);
-#pragma unroll
-    for (int h = 0; h < G; ++h) sh.pro.part[part][h][r] = acc[h];
-    __syncthreads();
-    for (int e = tid; e < G * kQjlDim; e += kThreads) {
-      const int h = e / kQjlDim, i = e % kQjlDim;
-      float v = 0.f;
-#pragma unroll
-      for (int pp = 0; pp < kParts; ++pp) v += sh.pro.part[pp][h][i];
-      sh.pro.s[h][i] = v;
-      slot[h * kQSlot + D + i] = v;
+    for (int pp = 0; pp < kParts; ++pp) {
+      v += sh.pro.part[pp][h][i];
+      if constexpr (QJL) w += sh.pro.part_s[pp][h][i];
     }
-    __syncthreads();
-    // lut[h][pos][nib] = sum_{k<4} s_h[4 pos + k] * (bit k of nib ? +1 : -1)
+    if constexpr (!KT::kOn) slot[i * G + h] = v;
+    sh.pro.qr[h][i] = v;
+    if constexpr (QJL) sh.pro.s[h][i] = w;
+  }
+  __syncthreads();
+  if constexpr (QJL) {
     for (int e = tid; e < G * kSignLut; e += kThreads) {
-      const int h = e / kSignLut, pos = (e % kSignLut) >> 4, nib = e & 15;
+      int pos, nib, h;
+      tab_entry<G>(e, pos, nib, h);
       float v = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) v += ((nib >> k) & 1) ? sh.pro.s[h][4 * pos + k] : -sh.pro.s[h][4 * pos + k];
-      s_slut[h][e % kSignLut] = v;
+      s_slut[e] = v;
+    }
+  }
+  if constexpr (KT::kOn) {
+    // centroid of code value c is coordinate 0 of dequantization entry c
+    for (int e = tid; e < KT::kFloats; e += kThreads) {
+      int pos, nib, h;
+      tab_entry<G>(e, pos, nib, h);
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < KT::kCpn; ++k)
+        v = fmaf(sh.pro.qr[h][KT::kCpn * pos + k], s_kdeq[((nib >> (KB * k)) & ((1 << KB) - 1)) * KL::kCoords], v);
+      s_ktab[e] = v;
     }
   }
   // The slot is re-read below through the scalar cache, which reads the L2 of
@@ -280,25 +402,29 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   // ------------------------------------------------------------ 1. main loop
   const uniform_fptr qs = (uniform_fptr)slot;
 
-  const int vstart = 2 * lane * VB;     // this lane owns rotated coordinates 2 lane, 2 lane + 1
-  const int vword = vstart >> 5;
-  const int vshift = vstart & 31;
-  const uint32_t vmask2 = (1u << (2 * VB)) - 1u;
-  uint32_t *rec = sh.vrec[wave];
+  // value sum layout: lane = (token group tg, coordinate group cg); the lane
+  // owns rotated coordinates 8 cg .. 8 cg + 7 and tokens 4 i + tg of a tile
+  const int cg = lane & 15, tg = lane >> 4;
+  const int vbit = 8 * VB * cg;
+  const int vword = vbit >> 5;
+  const int vshift = vbit & 31;
+  const uint32_t vmask8 = ((1u << (2 * VB)) - 1u) << 3;
+  uint32_t *rec = sh.loop.vrec[wave];
+  float *wts = sh.loop.wts[wave];
 
-  float m_run[G], l_run[G], acc0[G], acc1[G];
+  float m_run[G], l_lane[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-    acc0[h] = 0.f;
-    acc1[h] = 0.f;
+    l_lane[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[h][k] = 0.f;
   }
 
   for (int tb = tb0; tb < t_end; tb += kPass) {
     const int t = tb + lane;
     const bool valid = t < t_end;
-    if (tb != tb0) vcur = load_values(a, row_of(tb), VW);
+    if (tb != tb0) vcur = load_values(a, row0 + tb, t_end - tb, row_of(tb), VW, lane);
     KeyRegs<KW> nxt{};
     if (tb + kPass < t_end) nxt = load_keys<KW, QJL>(a, row_of(tb + kPass));
     float l[G];
@@ -323,10 +449,25 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
       // q~ comes from scalar loads of the slot; the pointer is re-laundered
       // every few coordinates (depending on the products two groups back) so
       // that only two groups of scalar values are live: one in use, one in flight.
+      if constexpr (KT::kOn) {
+        uint32_t tab_off = 0;   // always 0; opaque so that only kFlight positions of reads are in flight
+#pragma unroll
+        for (int p = 0; p < KT::kPos; ++p) {
+          if ((p % kFlight) == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) asm volatile("" : "+v"(tab_off) : "v"(dot[h]));
+          }
+          const uint32_t nib = ((kw[p >> 3] >> (4 * (p & 7))) & 15u) + tab_off;
+          float v[G];
+          tab_load<G>(s_ktab, p, nib, v);
+#pragma unroll
+          for (int h = 0; h < G; ++h) dot[h] += v[h];
+        }
+      }
       uniform_fptr qv = qs;
       constexpr int kRelaunder = (32 / G > KL::kCoords) ? 32 / G : KL::kCoords;
 #pragma unroll
-      for (int g = 0; g < KL::kLookups; ++g) {
+      for (int g = 0; g < (KT::kOn ? 0 : KL::kLookups); ++g) {
         const int c0 = g * KL::kCoords;
         if ((c0 % kRelaunder) == 0) {
 #pragma unroll
@@ -346,35 +487,38 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
           const float4 v = reinterpret_cast<const float4 *>(s_kdeq)[idx];
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            dot[h] = fmaf(qv[h * kQSlot + c0 + 0], v.x, dot[h]);
-            dot[h] = fmaf(qv[h * kQSlot + c0 + 1], v.y, dot[h]);
-            dot[h] = fmaf(qv[h * kQSlot + c0 + 2], v.z, dot[h]);
-            dot[h] = fmaf(qv[h * kQSlot + c0 + 3], v.w, dot[h]);
+            dot[h] = fmaf(qv[(c0 + 0) * G + h], v.x, dot[h]);
+            dot[h] = fmaf(qv[(c0 + 1) * G + h], v.y, dot[h]);
+            dot[h] = fmaf(qv[(c0 + 2) * G + h], v.z, dot[h]);
+            dot[h] = fmaf(qv[(c0 + 3) * G + h], v.w, dot[h]);
           }
         } else {
           const float2 v = reinterpret_cast<const float2 *>(s_kdeq)[idx];
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            dot[h] = fmaf(qv[h * kQSlot + c0 + 0], v.x, dot[h]);
-            dot[h] = fmaf(qv[h * kQSlot + c0 + 1], v.y, dot[h]);
+            dot[h] = fmaf(qv[(c0 + 0) * G + h], v.x, dot[h]);
+            dot[h] = fmaf(qv[(c0 + 1) * G + h], v.y, dot[h]);
           }
         }
       }
       if constexpr (QJL) {
+        // sign term: one table read per 4 signs gives all g heads' partial sums
         const uint32_t sw[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
         float sd[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) sd[h] = 0.f;
-        uint32_t lut_off = 0;   // always 0; opaque so that only 8 positions of loads are in flight
+        uint32_t lut_off = 0;   // always 0; opaque so that only kFlight positions of reads are in flight
 #pragma unroll
         for (int p = 0; p < 32; ++p) {
-          if ((p & 7) == 0) {
+          if ((p % kFlight) == 0) {
 #pragma unroll
             for (int h = 0; h < G; ++h) asm volatile("" : "+v"(lut_off) : "v"(sd[h]));
           }
           const uint32_t nib = ((sw[p >> 3] >> (4 * (p & 7))) & 15u) + lut_off;
+          float v[G];
+          tab_load<G>(s_slut, p, nib, v);
 #pragma unroll
-          for (int h = 0; h < G; ++h) sd[h] += s_slut[h][p * 16 + nib];
+          for (int h = 0; h < G; ++h) sd[h] += v[h];
         }
         const float gq = a.qjl_coef * gamma;
 #pragma unroll
@@ -387,55 +531,58 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
           a.dbg_scores[(static_cast<int64_t>(b) * a.n_q_heads + hq0 + h) * a.t_cap + t] = l[h];
       }
     }
-    // ---- stage this lane's value record
-    {
-      uint4 *dst = reinterpret_cast<uint4 *>(rec + lane * kRecStride);
+    // ---- online softmax (lazy running max)
+    bool grow = false;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        if (w < VW / 4) dst[w] = vcur.vc[w];
-      rec[lane * kRecStride + VW] = 0u;
+    for (int h = 0; h < G; ++h) grow = grow || (l[h] > m_run[h] + kLazy);
+    if (__any(grow)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float m_new = fmaxf(m_run[h], wave_max(l[h]));
+        const float alpha = (m_run[h] == -INFINITY) ? 0.f : __expf(m_run[h] - m_new);
+        m_run[h] = m_new;
+        l_lane[h] *= alpha;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[h][k] *= alpha;
+      }
     }
-    const float nu_v = vcur.nu_v;
-    // ---- online softmax over this wave's tile
     float w_tok[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mx = wave_max(l[h]);
-      const float m_new = fmaxf(m_run[h], mx);
-      const float alpha = (m_run[h] == -INFINITY) ? 0.f : __expf(m_run[h] - m_new);
-      const float p = valid ? __expf(l[h] - m_new) : 0.f;
-      l_run[h] = l_run[h] * alpha + wave_sum(p);
-      m_run[h] = m_new;
-      acc0[h] *= alpha;
-      acc1[h] *= alpha;
-      w_tok[h] = p * nu_v;   // zero for lanes past the end of the chunk
+      const float p = valid ? __expf(l[h] - m_run[h]) : 0.f;
+      l_lane[h] += p;
+      w_tok[h] = p * vcur.nu_v;   // zero for lanes past the end of the chunk
     }
+    // ---- stage the weights and the value records of this tile
+    lds_store_g<G>(wts + lane * G, w_tok);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (4 * k < VW) reinterpret_cast<uint4 *>(rec)[lane + 64 * k] = vcur.v[k];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- value sum over all 64 staged tokens (weights of missing tokens are 0)
-    for (int kb = 0; kb < 64; kb += 8) {
-      float2 v[8];
+    // ---- value sum: 16 tokens per lane, 8 coordinates x g heads each
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int tok = 4 * i + tg;
+      float wv[G];
+      lds_load_g<G>(wts + tok * G, wv);
+      const uint32_t w0 = rec[tok * VW + vword];
+      const uint32_t w1 = rec[tok * VW + vword + 1];
+      // byte offset of pair k in the table (8 bytes per entry) with one shift
+      // and one mask: pairs 0, 1 from the slice times 8 (they lie below bit
+      // 16, so nothing is shifted out), pairs 2, 3 from the slice shifted 3
+      // less to the right
+      const uint32_t slice = __builtin_amdgcn_alignbit(w1, w0, vshift);
+      const uint32_t slice8 = slice << 3;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t w0 = rec[(kb + u) * kRecStride + vword];
-        const uint32_t w1 = rec[(kb + u) * kRecStride + vword + 1];
-        const uint32_t win = __builtin_amdgcn_alignbit(w1, w0, vshift) & vmask2;
-        v[u] = s_vdeq[win];
-      }
-      // all the group's weights first, so that the scalar results are ready
-      // (no hazard stalls) by the time the products read them
-      float wk[8][G];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int h = 0; h < G; ++h) wk[u][h] = readlane_f(w_tok[h], kb + u);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t off = (k < 2 ? (slice8 >> (2 * VB * k)) : (slice >> (2 * VB * k - 3))) & vmask8;
+        const float2 c = *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(s_vdeq) + off);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          acc0[h] = fmaf(wk[u][h], v[u].x, acc0[h]);
-          acc1[h] = fmaf(wk[u][h], v[u].y, acc1[h]);
+          acc[h][2 * k] = fmaf(wv[h], c.x, acc[h][2 * k]);
+          acc[h][2 * k + 1] = fmaf(wv[h], c.y, acc[h][2 * k + 1]);
         }
       }
     }
@@ -446,11 +593,21 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   }
 
   // ------------------------------------------------------------ 2. merge waves
+  float l_wave[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l_wave[h] = wave_sum(l_lane[h]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc[h][k] += __shfl_xor(acc[h][k], 16);
+      acc[h][k] += __shfl_xor(acc[h][k], 32);
+    }
+  }
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       s_ml[wave][h][0] = m_run[h];
-      s_ml[wave][h][1] = l_run[h];
+      s_ml[wave][h][1] = l_wave[h];
     }
   }
   __syncthreads();   // every wave is done with its staged records
@@ -460,8 +617,10 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_ml[w][h][0]);
     const float f = (m_run[h] == -INFINITY) ? 0.f : __expf(m_run[h] - mx);
-    sh.merge[wave][h][2 * lane] = acc0[h] * f;
-    sh.merge[wave][h][2 * lane + 1] = acc1[h] * f;
+    if (tg == 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sh.merge[wave][h][8 * cg + k] = acc[h][k] * f;
+    }
   }
   __syncthreads();
   float *part_o = a.ws_part_o + static_cast<int64_t>(group_id) * G * D;
@@ -484,13 +643,15 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
     a.ws_part_ml[(static_cast<int64_t>(group_id) * G + h) * 2 + 0] = mx;
     a.ws_part_ml[(static_cast<int64_t>(group_id) * G + h) * 2 + 1] = lsum;
   }
-
 }
 
 // Merge of the chunks of one (b, q head): log-sum-exp weights, rotated sum,
 // then o = Pi_v^T o~.  A separate launch: the kernel boundary makes every
 // chunk's partials visible across XCDs without an in-kernel device fence.
+// Every global read (the chunks' (max, sum), their partial outputs and this
+// thread's slice of Pi_v) is issued before the first barrier.
 constexpr int kCombThreads = 512;
+constexpr int kCombPer = kMaxDecodeChunks / 4;   // partial outputs per thread
 
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
   __shared__ float s_w[kMaxDecodeChunks];
@@ -507,18 +668,24 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int nc = a.n_chunks;
   const int64_t grp0 = static_cast<int64_t>(row_id) * nc;
-  for (int c = tid; c < nc; c += kCombThreads) {
-    const float m = a.ws_part_ml[((grp0 + c) * g + h) * 2];
-    const float l = a.ws_part_ml[((grp0 + c) * g + h) * 2 + 1];
-    s_w[c] = (l > 0.f) ? m : -INFINITY;
-    s_l[c] = l;
-  }
-  // Prefetch Pi_v for the final product while the weights are computed:
-  // thread (i, quarter) covers j in [32 quarter, 32 quarter + 32).
+  // thread (i, quarter): output coordinate i; chunks quarter, quarter + 4, ...;
+  // Pi_v rows 32 quarter .. 32 quarter + 31 of column i
   const int i = tid & (D - 1), quarter = tid >> 7;
   float pv[32];
 #pragma unroll
   for (int jj = 0; jj < 32; ++jj) pv[jj] = a.rot_v[(32 * quarter + jj) * D + i];
+  float po[kCombPer];
+#pragma unroll
+  for (int k = 0; k < kCombPer; ++k) {
+    const int c = quarter + 4 * k;
+    po[k] = (c < nc) ? a.ws_part_o[((grp0 + c) * g + h) * D + i] : 0.f;
+  }
+  if (tid < nc) {
+    const float m = a.ws_part_ml[((grp0 + tid) * g + h) * 2];
+    const float l = a.ws_part_ml[((grp0 + tid) * g + h) * 2 + 1];
+    s_w[tid] = (l > 0.f) ? m : -INFINITY;
+    s_l[tid] = l;
+  }
   __syncthreads();
   if (tid < 64) {
     float mx = -INFINITY;
@@ -536,10 +703,12 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
   __syncthreads();
   const float inv = s_scal[0];
   {
-    // rotated output: thread (j, quarter) sums chunks c = quarter, quarter + 4, ...
     float o = 0.f;
-#pragma unroll 8
-    for (int c = quarter; c < nc; c += 4) o = fmaf(s_w[c], a.ws_part_o[((grp0 + c) * g + h) * D + i], o);
+#pragma unroll
+    for (int k = 0; k < kCombPer; ++k) {
+      const int c = quarter + 4 * k;
+      if (c < nc) o = fmaf(s_w[c], po[k], o);
+    }
     s_o[quarter][i] = o;
   }
   __syncthreads();
@@ -601,7 +770,7 @@ DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int64_t t_cap) 
   const int64_t groups = rows * p.n_chunks;
   auto align = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
   p.off_qslot = 0;
-  p.off_part_o = align(p.off_qslot + static_cast<size_t>(groups) * g * kQSlot * sizeof(float));
+  p.off_part_o = align(p.off_qslot + static_cast<size_t>(groups) * g * D * sizeof(float));
   p.off_part_ml = align(p.off_part_o + static_cast<size_t>(groups) * g * D * sizeof(float));
   p.total_bytes = align(p.off_part_ml + static_cast<size_t>(groups) * g * 2 * sizeof(float));
   return p;

@@ -40,14 +40,17 @@ namespace tq {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
+constexpr int kNT = 2;    // 16-vector MFMA column blocks per wave tile
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFragU4 = static_cast<int>(kFragBytesPerSplit / 16);  // uint4 per split
 
 __device__ __forceinline__ bf16x8 u4_as_bf16(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x2 u32_as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -60,8 +63,6 @@ __device__ __forceinline__ void split_bf16(const f32x8 &v, bf16x8 &hi, bf16x8 &l
   lo = __builtin_convertvector(v - back, bf16x8);
 }
 
-__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // One lane's 32 input coordinates of one vector.
 template <bool XF32> struct XRegs;
@@ -86,8 +87,9 @@ __device__ __forceinline__ void load_x(const EncodeArgs &a, int64_t tile, int j,
   }
 }
 
-template <int BITS, bool QJL, bool XF32, int NT>
+template <int BITS, bool QJL, bool XF32, bool DBG>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
+  constexpr int NT = kNT;
   __shared__ uint4 s_frag[(QJL ? 4 : 2) * kFragU4];
   __shared__ float4 s_qlut[kQuantCells];
 
@@ -117,31 +119,24 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     XRegs<XF32> cur[NT];
     load_x<XF32, NT>(a, tile, j, kk, cur);
 
-    int64_t vec[NT];
-    bool valid[NT];
     bf16x8 bx[NT][4];
-    bf16x8 bxlo[NT][4];
+    bf16x8 bxlo[XF32 ? NT : 1][4];
     float nu[NT], inv[NT];
 
     // ---- B operands and norms
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      vec[nt] = tile * (16 * NT) + nt * 16 + j;
-      valid[nt] = vec[nt] < n;
       float ss = 0.f;
       if constexpr (!XF32) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const uint4 w = cur[nt].w[s];
           bx[nt][s] = u4_as_bf16(w);
-          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const float v0 = bf16lo_to_f32(ws[h]);
-            const float v1 = bf16hi_to_f32(ws[h]);
-            ss = fmaf(v0, v0, ss);
-            ss = fmaf(v1, v1, ss);
-          }
+          // x_i^2 summed two at a time (bf16 products are exact in fp32)
+          ss = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(w.x), u32_as_bf16x2(w.x), ss, false);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(w.y), u32_as_bf16x2(w.y), ss, false);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(w.z), u32_as_bf16x2(w.z), ss, false);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(w.w), u32_as_bf16x2(w.w), ss, false);
         }
       } else {
 #pragma unroll
@@ -159,145 +154,177 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
       inv[nt] = (nu[nt] == 0.f) ? 0.f : 1.f / nu[nt];
     }
 
-    // ---- y = Pi x (M = output coordinate, N = vector, K = input coordinate);
-    // consecutive MFMAs always target different accumulators.
-    f32x4 acc[NT][8];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // keep the scheduler from hoisting every fragment load of the tile
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bf16x8 ah = u4_as_bf16(rot_hi[(t * 4 + s) * 64 + lane]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][t] = mfma(ah, bx[nt][s], acc[nt][t]);
-        if constexpr (XF32) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[nt][t] = mfma(ah, bxlo[nt][s], acc[nt][t]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bf16x8 al = u4_as_bf16(rot_lo[(t * 4 + s) * 64 + lane]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][t] = mfma(al, bx[nt][s], acc[nt][t]);
-      }
-    }
-
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- quantize, residual, pack (lane holds y[32kk + 4t + e] of vector vec[nt])
+    int64_t vec[NT];
+    bool valid[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      uint32_t words[BITS];
+      vec[nt] = tile * (16 * NT) + nt * 16 + j;
+      valid[nt] = vec[nt] < n;
+    }
+
+    // Output block t of y = Pi x (M = output coordinate, N = vector, K = input
+    // coordinate) gives the lane y[32 kk + 4 t + e] of vector vec[nt].
+    auto rotate_block = [&](int t, f32x4 (&acc)[NT]) {
 #pragma unroll
-      for (int w = 0; w < BITS; ++w) words[w] = 0u;
-      float rr = 0.f;
-      const bool dbg = a.dbg_rot != nullptr && valid[nt];
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        float yv[4];
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 ah = u4_as_bf16(rot_hi[(t * 4 + s) * 64 + lane]);
+        const bf16x8 al = u4_as_bf16(rot_lo[(t * 4 + s) * 64 + lane]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma(ah, bx[nt][s], acc[nt]);
+        if constexpr (XF32) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma(ah, bxlo[nt][s], acc[nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma(al, bx[nt][s], acc[nt]);
+      }
+    };
+
+    uint32_t words[NT][BITS];
+    float rr[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      rr[nt] = 0.f;
+#pragma unroll
+      for (int w = 0; w < BITS; ++w) words[nt][w] = 0u;
+    }
+    // Quantize, residual and pack of block t; the residual goes to rv.
+    auto quantize_block = [&](int t, f32x4 (&acc)[NT], float (&rv)[NT][4]) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float y = acc[nt][t][e] * inv[nt];
-          yv[e] = y;
-          // cell of y: thresholds below the cell are counted in q.x; q.y is the
-          // only threshold that may lie in the cell (NaN when none); q.z / q.w
-          // are the centroids below / above it.
+          const float y = acc[nt][e] * inv[nt];
+          // cell of y: q.x counts the thresholds below the cell; q.y is the only
+          // threshold that may lie in the cell (NaN when none); q.z / q.w are the
+          // centroids below / above it.
           const int cell = min(max(static_cast<int>(fmaf(y, qscale, qbias)), 0), kQuantCells - 1);
           const float4 q = s_qlut[cell];
           const bool up = y >= q.y;
           const uint32_t idx = __float_as_uint(q.x) + (up ? 1u : 0u);
           const int pos = (4 * t + e) * BITS;
-          words[pos / 32] |= idx << (pos % 32);
-          if ((pos % 32) + BITS > 32) words[pos / 32 + 1] |= idx >> (32 - (pos % 32));
+          words[nt][pos / 32] |= idx << (pos % 32);
+          if ((pos % 32) + BITS > 32) words[nt][pos / 32 + 1] |= idx >> (32 - (pos % 32));
           if constexpr (QJL) {
             const float r = y - (up ? q.w : q.z);
-            rr = fmaf(r, r, rr);
-            acc[nt][t][e] = r;   // keep the residual in place of y
+            rr[nt] = fmaf(r, r, rr[nt]);
+            rv[nt][e] = r;
+          }
+          if constexpr (DBG) acc[nt][e] = y;
+        }
+        if constexpr (DBG) {
+          if (a.dbg_rot != nullptr && valid[nt])
+            *reinterpret_cast<float4 *>(a.dbg_rot + vec[nt] * kHeadDim + 32 * kk + 4 * t) =
+                make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
+        }
+        // materialize the packed words now: otherwise the compiler sinks the
+        // packing into the final (conditional) store and keeps every
+        // coordinate's operands live until then
+#pragma unroll
+        for (int w = 0; w < BITS; ++w) asm volatile("" : "+v"(words[nt][w]));
+        if constexpr (QJL) asm volatile("" : "+v"(rr[nt]));
+      }
+    };
+
+    // QJL k-step s takes rotated coordinates 32 kk + 8 s .. + 7 of the lane,
+    // i.e. blocks 2 s and 2 s + 1: their residuals, split into bf16 hi and lo.
+    f32x4 pacc[QJL ? 8 : 1][NT];
+    if constexpr (QJL) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    auto qjl_step = [&](int s, const bf16x8 (&rh)[NT], const bf16x8 (&rl)[NT]) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const bf16x8 sh = u4_as_bf16(qjl_hi[(t * 4 + s) * 64 + lane]);
+        const bf16x8 sl = u4_as_bf16(qjl_lo[(t * 4 + s) * 64 + lane]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pacc[t][nt] = mfma(sh, rh[nt], pacc[t][nt]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pacc[t][nt] = mfma(sh, rl[nt], pacc[t][nt]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pacc[t][nt] = mfma(sl, rh[nt], pacc[t][nt]);
+      }
+    };
+
+    // ---- software pipeline over the 8 output blocks: step t quantizes block t
+    // (vector work) while the MFMAs of block t + 1 and, on even steps, of the
+    // QJL k-step whose residual pair was completed on the step before
+    // (independent of it) execute.
+    f32x4 racc[2][NT];
+    bf16x8 rh[QJL ? NT : 1], rl[QJL ? NT : 1];
+    float rpend[QJL ? NT : 1][4];
+    rotate_block(0, racc[0]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (t < 7) rotate_block(t + 1, racc[(t + 1) & 1]);
+      if constexpr (QJL) {
+        if (t >= 2 && (t & 1) == 0) qjl_step(t / 2 - 1, rh, rl);
+      }
+      float rv[NT][4];
+      quantize_block(t, racc[t & 1], rv);
+      if constexpr (QJL) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if ((t & 1) == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rpend[nt][e] = rv[nt][e];
+          } else {
+            const f32x8 v = {rpend[nt][0], rpend[nt][1], rpend[nt][2], rpend[nt][3], rv[nt][0], rv[nt][1], rv[nt][2], rv[nt][3]};
+            split_bf16(v, rh[nt], rl[nt]);
           }
         }
-        if (dbg)
-          *reinterpret_cast<float4 *>(a.dbg_rot + vec[nt] * kHeadDim + 32 * kk + 4 * t) =
-              make_float4(yv[0], yv[1], yv[2], yv[3]);
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (QJL) qjl_step(3, rh, rl);
+
+    // ---- emit codes, norms, residual norms
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       int64_t row = vec[nt];
       if (a.dst_row != nullptr) row = valid[nt] ? a.dst_row[vec[nt]] : -1;
       const bool ok = valid[nt] && row >= 0 && row < a.cache_rows;
+      if constexpr (QJL) {
+        rr[nt] += __shfl_xor(rr[nt], 16);
+        rr[nt] += __shfl_xor(rr[nt], 32);
+      }
       if (ok) {
         uint32_t *cp = a.codes + row * (4 * BITS) + kk * BITS;
         if constexpr (BITS == 4) {
-          *reinterpret_cast<uint4 *>(cp) = make_uint4(words[0], words[1], words[2], words[3]);
+          *reinterpret_cast<uint4 *>(cp) = make_uint4(words[nt][0], words[nt][1], words[nt][2], words[nt][3]);
         } else if constexpr (BITS == 2) {
-          *reinterpret_cast<uint2 *>(cp) = make_uint2(words[0], words[1]);
+          *reinterpret_cast<uint2 *>(cp) = make_uint2(words[nt][0], words[nt][1]);
         } else {
 #pragma unroll
-          for (int w = 0; w < BITS; ++w) cp[w] = words[w];
+          for (int w = 0; w < BITS; ++w) cp[w] = words[nt][w];
+        }
+        if (kk == 0) {
+          a.norms[row] = nu[nt];
+          if constexpr (QJL) a.res_norms[row] = sqrtf(rr[nt]);
         }
       }
       if constexpr (QJL) {
-        rr += __shfl_xor(rr, 16);
-        rr += __shfl_xor(rr, 32);
-        if (ok && kk == 0) a.res_norms[row] = sqrtf(rr);
-      }
-      if (ok && kk == 0) a.norms[row] = nu[nt];
-    }
-
-    if constexpr (QJL) {
-      // ---- p = S r (M = projection index, N = vector, K = rotated coordinate)
-      f32x4 accp[NT][8];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) accp[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 rh[NT], rl[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const f32x8 v = {acc[nt][2 * s][0],     acc[nt][2 * s][1],     acc[nt][2 * s][2],
-                           acc[nt][2 * s][3],     acc[nt][2 * s + 1][0], acc[nt][2 * s + 1][1],
-                           acc[nt][2 * s + 1][2], acc[nt][2 * s + 1][3]};
-          split_bf16(v, rh[nt], rl[nt]);
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 ah = u4_as_bf16(qjl_hi[(t * 4 + s) * 64 + lane]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) accp[nt][t] = mfma(ah, rh[nt], accp[nt][t]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) accp[nt][t] = mfma(ah, rl[nt], accp[nt][t]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 al = u4_as_bf16(qjl_lo[(t * 4 + s) * 64 + lane]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) accp[nt][t] = mfma(al, rh[nt], accp[nt][t]);
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        // sign word: bit (4t + e) = [p > 0]; built most significant bit first
+        // sign word bit (4 t + e) = [p > 0], built most significant bit first
         uint32_t sw = 0u;
 #pragma unroll
         for (int t = 7; t >= 0; --t)
 #pragma unroll
-          for (int e = 3; e >= 0; --e) sw = (sw << 1) | (accp[nt][t][e] > 0.f ? 1u : 0u);
-        if (a.dbg_proj != nullptr && valid[nt]) {
+          for (int e = 3; e >= 0; --e) sw = (sw << 1) | (pacc[t][nt][e] > 0.f ? 1u : 0u);
+        if constexpr (DBG) {
+          if (a.dbg_proj != nullptr && valid[nt]) {
 #pragma unroll
-          for (int t = 0; t < 8; ++t)
-            *reinterpret_cast<float4 *>(a.dbg_proj + vec[nt] * kQjlDim + 32 * kk + 4 * t) =
-                make_float4(accp[nt][t][0], accp[nt][t][1], accp[nt][t][2], accp[nt][t][3]);
+            for (int t = 0; t < 8; ++t)
+              *reinterpret_cast<float4 *>(a.dbg_proj + vec[nt] * kQjlDim + 32 * kk + 4 * t) =
+                  make_float4(pacc[t][nt][0], pacc[t][nt][1], pacc[t][nt][2], pacc[t][nt][3]);
+          }
         }
-        int64_t row = vec[nt];
-        if (a.dst_row != nullptr) row = valid[nt] ? a.dst_row[vec[nt]] : -1;
-        if (valid[nt] && row >= 0 && row < a.cache_rows) a.signs[row * (kQjlDim / 32) + kk] = sw;
+        if (ok) a.signs[row * (kQjlDim / 32) + kk] = sw;
       }
     }
   }
@@ -305,11 +332,16 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
 
 template <int BITS, bool QJL, bool XF32>
 hipError_t launch_t(const EncodeArgs &a, int num_cus, hipStream_t stream) {
-  constexpr int NT = 2;
-  const int64_t tiles = (a.n + 16 * NT - 1) / (16 * NT);
+  const int64_t tiles = (a.n + 16 * kNT - 1) / (16 * kNT);
   const int64_t wgs = (tiles + kWaves - 1) / kWaves;
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(wgs, num_cus)));
-  hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, NT>), dim3(grid), dim3(kThreads), 0, stream, a);
+  // Keys need the Pi and S fragments (128 KiB of LDS): one work-group per CU;
+  // values need only Pi's (64 KiB) and fewer registers: two per CU.
+  const int per_cu = QJL ? 1 : 2;
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(wgs, static_cast<int64_t>(num_cus) * per_cu)));
+  if (a.dbg_rot != nullptr || a.dbg_proj != nullptr)
+    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

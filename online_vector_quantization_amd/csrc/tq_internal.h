@@ -49,8 +49,7 @@ struct tq_codebook {
   size_t off_qjl_frag = 0;        // encode A-operand fragments of S: hi then lo
   size_t off_rot_f32 = 0;         // float[d*d] row-major Pi
   size_t off_rot_t_f32 = 0;       // float[d*d] row-major Pi^T
-  size_t off_qjl_f32 = 0;         // float[m*d] row-major S
-  size_t off_qjl_t_f32 = 0;       // float[d*m] row-major S^T
+  size_t off_qjl_rot_t_f32 = 0;   // float[d*m] row-major (S Pi)^T
   size_t off_key_lut = 0;         // decode key dequantization table
   size_t off_pair_lut = 0;        // decode value pair table
   size_t off_qcells = 0;          // encode quantizer cell table

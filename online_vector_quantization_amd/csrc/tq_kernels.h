@@ -68,7 +68,7 @@ constexpr size_t kPairLutBytes = 256 * 2 * sizeof(float);
 struct DecodePlan {
   int chunk;               // tokens per work-group chunk
   int n_chunks;
-  size_t off_qslot;        // bytes into the workspace: float[groups][g][d + 128], q~ and s per work-group
+  size_t off_qslot;        // bytes into the workspace: float[groups][d][g], q~ per work-group (coordinate-major)
   size_t off_part_o;       // float[groups][g][d]: rotated partial outputs
   size_t off_part_ml;      // float[groups][g][2]: running max and sum
   size_t total_bytes;
@@ -95,7 +95,7 @@ struct DecodeArgs {
   int out_bf16;
   float *dbg_scores;
   const float *rot_k_t;    // Pi_k^T row-major (d x d): entry [i][j] = Pi_k[j][i]
-  const float *qjl_t;      // S^T row-major (d x m)
+  const float *qjl_rot_t;  // (S Pi_k)^T row-major (d x m): s = S Pi_k q in one product
   const float *rot_v;      // Pi_v row-major (d x d)
   const float *k_lut;      // key dequantization table (kKeyLutBytes)
   const float *v_lut;      // value pair table (kPairLutBytes)
