@@ -37,9 +37,9 @@ HBM_PEAK_GBPS = 8000.0
 # --calib-copy 512, each scaled by the ratio of a 512 MiB device copy's known
 # bytes to what the same counter read for it.  Valid only for the encode
 # source they were taken on (sha256 below); otherwise reported as null.
-ENCODE_TRAFFIC = {"source_sha256": "e5948138fecbc9e4cc8b7f0a189e501e944ce3f8ac9bf165e7bb6ccac2fc7489",
+ENCODE_TRAFFIC = {"source_sha256": "78028214d8f86853d6c3476c48094b392f023f1bd6bc0fa53cbe35d5abc13f30",
                   "workload": "llama3-8b-layer-b1-s32768",
-                  "fetch_bytes": 68520455, "write_bytes": 14701427}
+                  "fetch_bytes": 68477913, "write_bytes": 14682167}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attn HBM GB/s (% of peak) on compressed KV; encode Mvectors/s"
 

@@ -92,7 +92,7 @@ tq_status upload_tables(tq_codebook *cb) {
   cb->off_pair_lut = off;
   off = align256(off + tq::kPairLutBytes);
   cb->off_qcells = off;
-  off = align256(off + tq::kQuantCells * 4 * sizeof(float));
+  off = align256(off + tq::kQuantCellEntries * 4 * sizeof(float));
   cb->dev_bytes = off;
 
   std::vector<unsigned char> img(off, 0);

@@ -56,6 +56,13 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// (w << 1) | [p > 0] as one compare and one add with carry.
+__device__ __forceinline__ uint32_t shift_in_positive(uint32_t w, float p) {
+  uint32_t r;
+  asm volatile("v_cmp_lt_f32 vcc, 0, %1\n\tv_addc_co_u32 %0, vcc, %2, %2, vcc" : "=v"(r) : "v"(p), "v"(w) : "vcc");
+  return r;
+}
+
 // Round 8 floats to bf16 (RNE) and return hi and lo = bf16(v - hi).
 __device__ __forceinline__ void split_bf16(const f32x8 &v, bf16x8 &hi, bf16x8 &lo) {
   hi = __builtin_convertvector(v, bf16x8);
@@ -91,14 +98,14 @@ template <int BITS, bool QJL, bool XF32, bool DBG>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   constexpr int NT = kNT;
   __shared__ uint4 s_frag[(QJL ? 4 : 2) * kFragU4];
-  __shared__ float4 s_qlut[kQuantCells];
+  __shared__ float4 s_qlut[kQuantCellEntries];
 
   const int tid = threadIdx.x;
   for (int i = tid; i < 2 * kFragU4; i += kThreads) s_frag[i] = a.frag_rot[i];
   if constexpr (QJL) {
     for (int i = tid; i < 2 * kFragU4; i += kThreads) s_frag[2 * kFragU4 + i] = a.frag_qjl[i];
   }
-  for (int i = tid; i < kQuantCells; i += kThreads) s_qlut[i] = a.qlut[i];
+  for (int i = tid; i < kQuantCellEntries; i += kThreads) s_qlut[i] = a.qlut[i];
   __syncthreads();
 
   const uint4 *rot_hi = s_frag;
@@ -200,7 +207,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
           // cell of y: q.x counts the thresholds below the cell; q.y is the only
           // threshold that may lie in the cell (NaN when none); q.z / q.w are the
           // centroids below / above it.
-          const int cell = min(max(static_cast<int>(fmaf(y, qscale, qbias)), 0), kQuantCells - 1);
+          // |y| <= 1 up to rounding gives cells 0 .. kQuantCells; the clamp only
+          // matters for inputs whose norm is lost to underflow
+          const uint32_t cell = min(__float2uint_rz(fmaf(y, qscale, qbias)), static_cast<uint32_t>(kQuantCellEntries - 1));
           const float4 q = s_qlut[cell];
           const bool up = y >= q.y;
           const uint32_t idx = __float_as_uint(q.x) + (up ? 1u : 0u);
@@ -315,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
 #pragma unroll
         for (int t = 7; t >= 0; --t)
 #pragma unroll
-          for (int e = 3; e >= 0; --e) sw = (sw << 1) | (pacc[t][nt][e] > 0.f ? 1u : 0u);
+          for (int e = 3; e >= 0; --e) sw = shift_in_positive(sw, pacc[t][nt][e]);
         if constexpr (DBG) {
           if (a.dbg_proj != nullptr && valid[nt]) {
 #pragma unroll
@@ -375,17 +384,20 @@ void pack_encode_fragments(const float *mat, void *dst) {
 
 bool build_quant_cells(const float *thresholds, const float *centroids, int levels, float *cells,
                        float *qscale, float *qbias) {
-  // Cells of width w over [-Y, Y) with Y = 0.5; the kernel computes
-  // cell = clamp(int(y * K/(2Y) + K/2), 0, K-1).  For each cell: the count of
-  // thresholds below (lo - eps), the single threshold in [lo - eps, hi + eps]
-  // (NaN if none) and the centroids on either side of it.  eps covers the
-  // rounding of the cell computation; more than one candidate fails the build.
-  const double Y = 0.5, w = 2.0 * Y / kQuantCells, eps = 0.05 * w;
+  // Cells of width w = 2/K over [-1, 1]; the kernel computes
+  // cell = min(uint(y * K/2 + K/2), entries - 1) (truncating, negative -> 0,
+  // NaN -> 0).  A rotated unit vector has |y| <= 1 up to rounding, so cells
+  // 0 .. K (K: y at or just above 1) are what occur; the guard entries past K
+  // repeat the last cell.  For each cell: the count of thresholds below (lo - eps), the
+  // single threshold in [lo - eps, hi + eps] (NaN if none) and the centroids
+  // on either side of it.  eps covers the rounding of the cell computation;
+  // more than one candidate fails the build.
+  const double w = 2.0 / kQuantCells, eps = 0.05 * w;
   const int nt = levels - 1;
   for (int i = 0; i < nt; ++i)
-    if (!(std::fabs(thresholds[i]) < Y - 2 * w)) return false;
-  for (int k = 0; k < kQuantCells; ++k) {
-    const double lo = -Y + k * w, hi = lo + w;
+    if (!(std::fabs(thresholds[i]) < 1.0 - 2 * w)) return false;
+  for (int k = 0; k < kQuantCellEntries; ++k) {
+    const double lo = -1.0 + std::min(k, kQuantCells) * w, hi = lo + w;
     int below = 0, cand = -1, ncand = 0;
     for (int i = 0; i < nt; ++i) {
       if (thresholds[i] < lo - eps) {
@@ -402,7 +414,7 @@ bool build_quant_cells(const float *thresholds, const float *centroids, int leve
     cells[4 * k + 2] = centroids[below];
     cells[4 * k + 3] = centroids[std::min(below + 1, levels - 1)];
   }
-  *qscale = static_cast<float>(kQuantCells / (2.0 * Y));
+  *qscale = static_cast<float>(kQuantCells / 2.0);
   *qbias = static_cast<float>(kQuantCells / 2.0);
   return true;
 }

@@ -18,8 +18,10 @@ constexpr int kMaxLevels = 16;   // 2^4
 constexpr size_t kFragBytesPerSplit = 8 * 4 * 64 * 16;   // 32 KiB
 constexpr size_t kFragBytes = 2 * kFragBytesPerSplit;     // hi + lo
 
-// Quantizer cell table: kQuantCells float4 entries (see build_quant_cells).
+// Quantizer cell table: kQuantCells cells over [-1, 1] plus guard entries,
+// kQuantCellEntries float4 entries in all (see build_quant_cells).
 constexpr int kQuantCells = 512;
+constexpr int kQuantCellEntries = kQuantCells + 8;
 
 struct EncodeArgs {
   const void *x;
@@ -35,8 +37,8 @@ struct EncodeArgs {
   float *dbg_proj;
   const uint4 *frag_rot;   // kFragBytes
   const uint4 *frag_qjl;   // kFragBytes (keys with QJL)
-  const float4 *qlut;      // kQuantCells quantizer cells
-  float qscale, qbias;     // cell = clamp(int(y * qscale + qbias), 0, kQuantCells - 1)
+  const float4 *qlut;      // kQuantCellEntries quantizer cells
+  float qscale, qbias;     // cell = min(uint(y * qscale + qbias), kQuantCellEntries - 1)
 };
 
 // Fills `dst` (kFragBytes) with the hi/lo bf16 fragments of the 128 x 128
