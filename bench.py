@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama8b", choices=["llama8b", "llama70b", "batched2", "batched4"])
     ap.add_argument("--hot", action="store_true", help="no replica rotation (cache-resident numbers)")
+    ap.add_argument("--key-mode", default="qjl", choices=["qjl", "mse"],
+                    help="keys as (b-1)-bit codes + 1-bit QJL (default) or b-bit MSE-only codes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle step until this much CPU time has run")
@@ -90,7 +92,10 @@ def main():
     kbits_mse = wl.k_bits - 1
     print(f"[bench] workload {wl.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    kcb = T.Codebook(128, kbits_mse, 128, 0, 1, device=0)
+    if args.key_mode == "mse":
+        kbits_mse = wl.k_bits
+    qjl_m = 128 if args.key_mode == "qjl" else 0
+    kcb = T.Codebook(128, kbits_mse, qjl_m, 0, 1, device=0)
     vcb = T.Codebook(128, wl.v_bits, 0, 0, 1, device=0)
     n_vec = B * Hkv * S
 
@@ -169,13 +174,13 @@ def main():
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
     enc_ms = float((enc_k + enc_v).mean())
     enc_mvps = 2 * n_vec / (enc_ms * 1e-3) / 1e6
-    k_rec = 4 * kcb.code_words + 4 * kcb.sign_words + 8
+    k_rec = 4 * kcb.code_words + 4 * kcb.sign_words + 4 + (4 if qjl_m else 0)
     v_rec = 4 * vcb.code_words + 4
     enc_k_bytes = n_vec * (256 + k_rec)
     enc_v_bytes = n_vec * (256 + v_rec)
     enc_k_gbps = enc_k_bytes / (enc_k.mean() * 1e-3) / 1e9
     enc_v_gbps = enc_v_bytes / (enc_v.mean() * 1e-3) / 1e9
-    enc_k_tflops = n_vec * 2 * 128 * (128 + 128) / (enc_k.mean() * 1e-3) / 1e12
+    enc_k_tflops = n_vec * 2 * 128 * (128 + qjl_m) / (enc_k.mean() * 1e-3) / 1e12
 
     line = {
         "metric": METRIC,
@@ -192,7 +197,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name, "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
-            "key_bits": wl.k_bits, "value_bits": wl.v_bits, "qjl_dim": 128, "input_dtype": "bf16",
+            "key_bits": wl.k_bits, "value_bits": wl.v_bits, "qjl_dim": qjl_m, "input_dtype": "bf16",
+            "key_mode": "(b-1)-bit codes + 1-bit QJL" if qjl_m else "b-bit MSE-only codes",
             "step": "encode all K and V of the layer, then one decode step over a full cache",
             "cold_replicas": {"inputs": n_in, "caches": n_cache, "hot": bool(args.hot)},
         },
@@ -201,9 +207,9 @@ def main():
         "encode_mvectors_per_s": round(enc_mvps, 1),
         "encode_us": {"keys": round(float(enc_k.mean()) * 1e3, 2), "values": round(float(enc_v.mean()) * 1e3, 2)},
         "roofline": {
-            "kernel": "encode (keys: rotation + QJL)", "bound": "hbm",
+            "kernel": "encode (keys: rotation + QJL)" if qjl_m else "encode (keys: rotation, MSE-only)", "bound": "hbm",
             "achieved": round(enc_k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4), "traffic": encode_traffic(wl.name),
+            "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4), "traffic": encode_traffic(wl.name) if qjl_m else None,
             "algorithmic_bytes_per_launch": enc_k_bytes, "avg_launch_us": round(float(enc_k.mean()) * 1e3, 2),
             "mfma_tflops_algorithmic": round(enc_k_tflops, 1),
         },
@@ -220,7 +226,7 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, qjl=bool(qjl_m))
     print(json.dumps(line), flush=True)
 
 
@@ -238,7 +244,7 @@ def encode_traffic(workload_name):
     return t["fetch_bytes"] + t["write_bytes"]
 
 
-def cpu_baseline(wl, min_seconds):
+def cpu_baseline(wl, min_seconds, qjl=True):
     """The CPU oracle (float64 numpy) on the same step: encode every K and V
     vector of the layer, then decode all q heads over the full cache.  The step
     is repeated until at least `min_seconds` of CPU work have run."""
@@ -250,11 +256,11 @@ def cpu_baseline(wl, min_seconds):
     except Exception:
         blas_threads = 1
     B, Hkv, S = wl.batch, wl.n_kv_heads, wl.seq_len
-    kb = wl.k_bits - 1
+    kb = wl.k_bits - 1 if qjl else wl.k_bits
     c_k, t_k = O.build_codebook(128, kb)
     c_v, t_v = O.build_codebook(128, wl.v_bits)
     Pi = O.haar_rotation(128, 0)
-    Sm = O.qjl_matrix(128, 128, 1)
+    Sm = O.qjl_matrix(128, 128, 1) if qjl else None
     kx = synth.bf16_to_f32(wl.k.reshape(-1, 128))
     vx = synth.bf16_to_f32(wl.v.reshape(-1, 128))
     qh = synth.bf16_to_f32(wl.q).astype(np.float64)
@@ -266,8 +272,8 @@ def cpu_baseline(wl, min_seconds):
         ek = O.encode(kx, Pi, c_k, t_k, Sm)
         ev = O.encode(vx, Pi, c_v, t_v)
         kcache = {"codes": O.pack_bits(ek["idx"], kb).reshape(*shape, -1),
-                  "signs": O.pack_bits(ek["z"], 1).reshape(*shape, -1),
-                  "norms": ek["nu"].reshape(shape), "res_norms": ek["gamma"].reshape(shape)}
+                  "signs": O.pack_bits(ek["z"], 1).reshape(*shape, -1) if qjl else None,
+                  "norms": ek["nu"].reshape(shape), "res_norms": ek["gamma"].reshape(shape) if qjl else None}
         vcache = {"codes": O.pack_bits(ev["idx"], wl.v_bits).reshape(*shape, -1), "norms": ev["nu"].reshape(shape)}
         t1 = time.perf_counter()
         O.decode_attention(qh, kcache, vcache, [S] * B, {"bits": kb, "centroids": c_k, "Pi": Pi, "S": Sm},
@@ -277,7 +283,7 @@ def cpu_baseline(wl, min_seconds):
         t_dec += t2 - t1
         reps += 1
     n_vec = B * Hkv * S
-    rec = (4 * 4 * kb + 16 + 8) + (4 * 4 * wl.v_bits + 4)
+    rec = (4 * 4 * kb + (16 + 8 if qjl else 4)) + (4 * 4 * wl.v_bits + 4)
     dec_gbps = reps * n_vec * rec / t_dec / 1e9
     return {"value": round(dec_gbps, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
             "encode_mvectors_per_s": round(reps * 2 * n_vec / t_enc / 1e6, 4),

@@ -383,6 +383,26 @@ def test_one_bit_mse_inner_product_bias(golden_dir):
     assert abs(slope - g["one_bit_inner_product_bias"]) < 0.02
 
 
+def test_mse_inner_product_slope_is_one_minus_distortion():
+    # Centroid condition: E[y Q(y)] = E[Q(y)^2], so for a rotation-invariant
+    # key law E<q, k_hat> = (1 - D) <q, k> exactly, at every width (the 1-bit
+    # case is the 2/pi shrinkage above); the slope over 20000 keys must match.
+    d = 128
+    Pi = O.haar_rotation(d, 0)
+    rng = np.random.default_rng(13)
+    k = rng.standard_normal((20000, d))
+    q = rng.standard_normal(d)
+    exact = k @ q
+    for bits in (1, 2, 3, 4):
+        c, t = O.build_codebook(d, bits)
+        D = O.codebook_distortion(d, c.astype(np.float64), t.astype(np.float64))
+        e = O.encode(k, Pi, c, t)
+        est = ((c.astype(np.float64)[e["idx"]] @ Pi) * e["nu"][:, None]) @ q
+        slope = (est @ exact) / (exact @ exact)
+        se = math.sqrt((est - slope * exact).var() / (exact @ exact))
+        assert abs(slope - (1.0 - D)) < 4.0 * se
+
+
 # ---------------------------------------------------------------- decode
 
 def _lossless_cache(rng, B, Hkv, T, d, kbits, vbits, Pi):
