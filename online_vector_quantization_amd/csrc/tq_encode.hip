@@ -43,10 +43,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 8;
 constexpr int kNT = 2;    // 16-vector MFMA column blocks per wave tile
-constexpr int kThreads = 64 * kWaves;
+// Waves per work-group (keys: one work-group per CU, 128 KiB of LDS for the
+// Pi and S fragments; values: two per CU, 64 KiB).  Twelve-wave key groups
+// (three waves per SIMD) were measured slower: their register budget of 168
+// forces spills.
+template <bool QJL> struct EncGeom {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = 64 * kWaves;
+};
 constexpr int kFragU4 = static_cast<int>(kFragBytesPerSplit / 16);  // uint4 per split
 
 __device__ __forceinline__ bf16x8 u4_as_bf16(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -64,10 +71,21 @@ __device__ __forceinline__ uint32_t shift_in_positive(uint32_t w, float p) {
 }
 
 // Round 8 floats to bf16 (RNE) and return hi and lo = bf16(v - hi).
+// The rounded pairs are unpacked back to fp32 with a shift and a mask (the
+// generic conversion would round each element a second time).
 __device__ __forceinline__ void split_bf16(const f32x8 &v, bf16x8 &hi, bf16x8 &lo) {
-  hi = __builtin_convertvector(v, bf16x8);
-  const f32x8 back = __builtin_convertvector(hi, f32x8);
-  lo = __builtin_convertvector(v - back, bf16x8);
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t hp = __builtin_convertvector((f32x2){v[2 * p], v[2 * p + 1]}, bf16x2_t);
+    h[p] = __builtin_bit_cast(uint32_t, hp);
+    const float b0 = __uint_as_float(h[p] << 16), b1 = __uint_as_float(h[p] & 0xffff0000u);
+    const bf16x2_t lp = __builtin_convertvector((f32x2){v[2 * p] - b0, v[2 * p + 1] - b1}, bf16x2_t);
+    l[p] = __builtin_bit_cast(uint32_t, lp);
+  }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 
@@ -95,8 +113,10 @@ __device__ __forceinline__ void load_x(const EncodeArgs &a, int64_t tile, int j,
 }
 
 template <int BITS, bool QJL, bool XF32, bool DBG>
-__global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(EncGeom<QJL>::kThreads) void encode_kernel(EncodeArgs a) {
   constexpr int NT = kNT;
+  constexpr int kWaves = EncGeom<QJL>::kWaves;
+  constexpr int kThreads = EncGeom<QJL>::kThreads;
   __shared__ uint4 s_frag[(QJL ? 4 : 2) * kFragU4];
   __shared__ float4 s_qlut[kQuantCellEntries];
 
@@ -108,14 +128,16 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   for (int i = tid; i < kQuantCellEntries; i += kThreads) s_qlut[i] = a.qlut[i];
   __syncthreads();
 
-  const uint4 *rot_hi = s_frag;
-  const uint4 *rot_lo = s_frag + kFragU4;
-  const uint4 *qjl_hi = s_frag + 2 * kFragU4;
-  const uint4 *qjl_lo = s_frag + 3 * kFragU4;
 
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int j = lane & 15;
+  // Per-lane fragment indices for the Pi and S halves of LDS, opaque to the
+  // compiler: every fragment read is then one base register plus an
+  // immediate offset (S's half lies beyond the 64 KiB immediate range of
+  // the s_frag base, which otherwise costs a register per fragment).
+  uint32_t rot_l = lane, qjl_l = lane + 2 * kFragU4;
+  asm volatile("" : "+v"(rot_l), "+v"(qjl_l));
   const int kk = lane >> 4;
   const int64_t n = a.n;
   const int64_t tiles = (n + 16 * NT - 1) / (16 * NT);
@@ -176,8 +198,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
       for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 ah = u4_as_bf16(rot_hi[(t * 4 + s) * 64 + lane]);
-        const bf16x8 al = u4_as_bf16(rot_lo[(t * 4 + s) * 64 + lane]);
+        const bf16x8 ah = u4_as_bf16(s_frag[rot_l + (t * 4 + s) * 64]);
+        const bf16x8 al = u4_as_bf16(s_frag[rot_l + kFragU4 + (t * 4 + s) * 64]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma(ah, bx[nt][s], acc[nt]);
         if constexpr (XF32) {
@@ -249,8 +271,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     auto qjl_step = [&](int s, const bf16x8 (&rh)[NT], const bf16x8 (&rl)[NT]) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const bf16x8 sh = u4_as_bf16(qjl_hi[(t * 4 + s) * 64 + lane]);
-        const bf16x8 sl = u4_as_bf16(qjl_lo[(t * 4 + s) * 64 + lane]);
+        const bf16x8 sh = u4_as_bf16(s_frag[qjl_l + (t * 4 + s) * 64]);
+        const bf16x8 sl = u4_as_bf16(s_frag[qjl_l + kFragU4 + (t * 4 + s) * 64]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) pacc[t][nt] = mfma(sh, rh[nt], pacc[t][nt]);
 #pragma unroll
@@ -342,15 +364,16 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
 template <int BITS, bool QJL, bool XF32>
 hipError_t launch_t(const EncodeArgs &a, int num_cus, hipStream_t stream) {
   const int64_t tiles = (a.n + 16 * kNT - 1) / (16 * kNT);
+  constexpr int kWaves = EncGeom<QJL>::kWaves;
   const int64_t wgs = (tiles + kWaves - 1) / kWaves;
   // Keys need the Pi and S fragments (128 KiB of LDS): one work-group per CU;
   // values need only Pi's (64 KiB) and fewer registers: two per CU.
   const int per_cu = QJL ? 1 : 2;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(wgs, static_cast<int64_t>(num_cus) * per_cu)));
   if (a.dbg_rot != nullptr || a.dbg_proj != nullptr)
-    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, true>), dim3(grid), dim3(EncGeom<QJL>::kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, false>), dim3(grid), dim3(EncGeom<QJL>::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
