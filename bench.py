@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama8b", choices=["llama8b", "llama70b", "batched2", "batched4"])
     ap.add_argument("--hot", action="store_true", help="no replica rotation (cache-resident numbers)")
+    ap.add_argument("--append-steps", type=int, default=0, metavar="N",
+                    help="also time N decode-loop steps (append one token per sequence and head, then attend): "
+                         "separate calls, tq_append_decode, and one captured step replayed as a graph")
     ap.add_argument("--key-mode", default="qjl", choices=["qjl", "mse"],
                     help="keys as (b-1)-bit codes + 1-bit QJL (default) or b-bit MSE-only codes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -225,9 +228,93 @@ def main():
         },
         "wall_s_timed": round(wall, 4),
     }
+    if args.append_steps > 0:
+        line["append_step_us"] = append_steps(wl, kcb, vcb, up, args.append_steps, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, qjl=bool(qjl_m))
     print(json.dumps(line), flush=True)
+
+
+def append_steps(wl, kcb, vcb, up, steps, dev):
+    """Per-step time of a decode loop over the workload's caches (prefilled with
+    seq_len tokens, capacity seq_len + steps): each step appends one key and
+    value per (sequence, kv head) and attends the step's queries over the grown
+    cache.  Three ways: separate calls (host-built destination rows, two encodes,
+    a decode), tq_append_decode, and one captured append step replayed as a
+    graph.  The caches stay resident (no replica rotation)."""
+    import torch
+    import online_vector_quantization_amd as T
+    from online_vector_quantization_amd import synth
+    B, Hq, Hkv, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.seq_len
+    t_cap = S + steps
+    kc = T.CompressedCache.allocate(kcb, B, Hkv, t_cap)
+    vc = T.CompressedCache.allocate(vcb, B, Hkv, t_cap)
+    bb, hh, tt = torch.meshgrid(torch.arange(B), torch.arange(Hkv), torch.arange(S), indexing="ij")
+    dst = ((bb * Hkv + hh) * t_cap + tt).reshape(-1).to(dev)
+    T.encode_into_cache(kcb, up(wl.k), kc, dst_row=dst)
+    T.encode_into_cache(vcb, up(wl.v), vc, dst_row=dst)
+    del dst
+    ins = []
+    for s in range(steps):
+        ka, va, qa = synth.appended_tokens(s, batch=B) if B == 16 else (None, None, None)
+        if ka is None:
+            rng = np.random.default_rng(1000 + s)
+            ka = synth.bf16_bits(rng.standard_normal((B, Hkv, 1, 128), dtype=np.float32))
+            va = synth.bf16_bits(rng.standard_normal((B, Hkv, 1, 128), dtype=np.float32))
+            qa = synth.bf16_bits(rng.standard_normal((B, Hq, 128), dtype=np.float32))
+        tob = lambda a, shape: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev).reshape(shape)
+        ins.append((tob(ka, (B, Hkv, 128)), tob(va, (B, Hkv, 128)), tob(qa, (B, Hq, 128))))
+    ws = T.alloc_workspace(B, Hq, Hkv, t_cap, dev)
+    out = torch.empty(B, Hq, 128, dtype=torch.bfloat16, device=dev)
+    seq = torch.full((B,), S, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(run):
+        seq.fill_(S)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(steps):
+            run(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    def separate(s):
+        kn, vn, q = ins[s]
+        rows = torch.tensor([(b * Hkv + h) * t_cap + S + s for b in range(B) for h in range(Hkv)],
+                            dtype=torch.int64).to(dev, non_blocking=False)
+        T.encode_into_cache(kcb, kn.reshape(-1, 128), kc, dst_row=rows, stream=stream)
+        T.encode_into_cache(vcb, vn.reshape(-1, 128), vc, dst_row=rows, stream=stream)
+        sl = torch.full((B,), S + s + 1, dtype=torch.int32, device=dev)
+        T.decode_attention(kcb, vcb, q, kc, vc, sl, out=out, workspace=ws, stream=stream)
+
+    def fused(s):
+        kn, vn, q = ins[s]
+        T.append_decode(kcb, vcb, kn, vn, q, kc, vc, seq, out=out, workspace=ws, stream=stream)
+
+    kn_s = torch.empty_like(ins[0][0]); vn_s = torch.empty_like(ins[0][1]); q_s = torch.empty_like(ins[0][2])
+    timed(fused)                                     # warm-up
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side), torch.cuda.graph(graph, stream=side):
+        T.append_decode(kcb, vcb, kn_s, vn_s, q_s, kc, vc, seq, out=out, workspace=ws, stream=side)
+    stream.wait_stream(side)
+
+    def replay(s):
+        graph.replay()
+
+    # the graph's static inputs hold step 0's token (in a serving loop the
+    # projections that produce k, v, q would write them there)
+    kn_s.copy_(ins[0][0]); vn_s.copy_(ins[0][1]); q_s.copy_(ins[0][2])
+    res = {"steps": steps, "separate_calls": round(timed(separate), 2), "append_decode": round(timed(fused), 2),
+           "append_decode_graph": round(timed(replay), 2),
+           "decode_only": round(timed(lambda s: T.decode_attention(kcb, vcb, ins[s][2], kc, vc, seq, out=out,
+                                                                     workspace=ws, stream=stream)), 2),
+           "cache": "resident (no replica rotation)",
+           "note": "graph replays reuse one step's inputs, already in the captured buffers"}
+    return res
 
 
 def encode_traffic(workload_name):

@@ -172,6 +172,31 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
                               tq_dtype out_dtype, float *dbg_scores, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* One step of a decode loop, enqueued on `stream` with no host synchronization
+ * (so a caller can capture it in a graph and replay it): the new key and value
+ * of every (b, kv head) are appended to the caches, the queries attend over
+ * the grown cache, and seq_len grows by one [admirer.cn memory-wall article,
+ * section 1: each generated token appends its K and V and attends over all of
+ * them; intelliparadigm "3-bit" article, section 3.2: the cache is written
+ * sequentially and read at attention].
+ *   k_new, v_new  device [batch][n_kv_heads][d] of kv_dtype (contiguous); row
+ *                 (b, h) is encoded into cache row (b*n_kv_heads + h)*t_cap +
+ *                 seq_len[b] of k and v (keys with kcb, values with vcb).
+ *   seq_len       device int32[batch], read and then advanced on the device:
+ *                 a sequence with 0 <= seq_len[b] < t_cap gets the new token
+ *                 and seq_len[b] + 1; one at t_cap (full) attends over its t_cap
+ *                 tokens and is neither written nor advanced.
+ *   k, v          the caches, written at the appended rows (the const in
+ *                 tq_cache does not apply here).
+ * Other arguments as in tq_decode_attention (no dbg_scores).  Results equal
+ * tq_encode_kv of the new rows into those rows followed by tq_decode_attention
+ * with seq_len + 1, bit for bit. */
+tq_status tq_append_decode(const tq_codebook *kcb, const tq_codebook *vcb, const void *k_new, const void *v_new,
+                           tq_dtype kv_dtype, const void *q, tq_dtype q_dtype, const tq_cache *k, const tq_cache *v,
+                           int32_t *seq_len, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                           float softmax_scale, void *out, tq_dtype out_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Static name of a status code. */
 const char *tq_status_string(tq_status s);
 

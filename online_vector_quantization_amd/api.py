@@ -24,7 +24,7 @@ TQ_F32, TQ_BF16 = 0, 1
 EXPORTED = (
     "tq_codebook_build", "tq_codebook_free", "tq_codebook_info", "tq_codebook_export",
     "tq_codebook_export_f64", "tq_record_words", "tq_encode_kv", "tq_decode_workspace_bytes",
-    "tq_decode_attention", "tq_status_string", "tq_last_error",
+    "tq_decode_attention", "tq_append_decode", "tq_status_string", "tq_last_error",
 )
 
 
@@ -62,6 +62,8 @@ def load_library() -> ctypes.CDLL:
     lib.tq_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_decode_attention.argtypes = [vp, vp, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache), vp,
                                         i32, i32, i32, f32, vp, i32, vp, vp, ctypes.c_size_t, vp]
+    lib.tq_append_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache),
+                                     vp, i32, i32, i32, f32, vp, i32, vp, ctypes.c_size_t, vp]
     for name in EXPORTED:
         if name not in ("tq_status_string", "tq_last_error"):
             getattr(lib, name).restype = ctypes.c_int
@@ -254,6 +256,36 @@ def decode_attention(kcb: Codebook, vcb: Codebook, q: torch.Tensor, kcache: Comp
         kcb.handle, vcb.handle, _ptr(q), _dtype_code(q), ctypes.byref(ks), ctypes.byref(vs), _ptr(seq_len),
         B, Hq, Hkv, float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(dbg_scores), _ptr(workspace),
         workspace.numel(), _stream_handle(stream, q.device)), "tq_decode_attention")
+    return out
+
+
+def append_decode(kcb: Codebook, vcb: Codebook, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                  kcache: CompressedCache, vcache: CompressedCache, seq_len: torch.Tensor,
+                  out: Optional[torch.Tensor] = None, softmax_scale: float = 0.0, out_dtype=torch.float32,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tq_append_decode: append k_new/v_new [B, Hkv, d] at position seq_len[b], attend q [B, Hq, d]
+    over the grown caches, advance seq_len on the device.  No host synchronization."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, d] tensor")
+    B, Hq, d = q.shape
+    Hkv = kcache.codes.shape[1]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.shape != (B, Hkv, d) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, Hkv, d] tensor")
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must share a dtype")
+    if seq_len.dtype != torch.int32 or seq_len.numel() != B or not seq_len.is_contiguous():
+        raise ValueError("seq_len must be a contiguous int32 tensor with B entries")
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=out_dtype, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, kcache.t_cap, q.device)
+    _require_cuda(q, k_new, v_new, seq_len, out, workspace, kcache.codes, vcache.codes)
+    ks, vs = kcache.as_struct(), vcache.as_struct()
+    _check(load_library().tq_append_decode(
+        kcb.handle, vcb.handle, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(q), _dtype_code(q),
+        ctypes.byref(ks), ctypes.byref(vs), _ptr(seq_len), B, Hq, Hkv, float(softmax_scale), _ptr(out),
+        _dtype_code(out), _ptr(workspace), workspace.numel(), _stream_handle(stream, q.device)), "tq_append_decode")
     return out
 
 

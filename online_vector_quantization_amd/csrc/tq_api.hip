@@ -240,15 +240,20 @@ tq_status tq_record_words(const tq_codebook *cb, int32_t *code_words, int32_t *s
   return ok();
 }
 
-tq_status tq_encode_kv(const tq_codebook *cb, const void *x, tq_dtype x_dtype, int64_t n, int64_t x_row_stride,
-                       const int64_t *dst_row, int64_t cache_rows, uint32_t *codes, uint32_t *signs, float *norms,
-                       float *res_norms, float *dbg_rot, float *dbg_proj, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch arguments of an encode (no launch).
+tq_status prepare_encode(const tq_codebook *cb, const void *x, tq_dtype x_dtype, int64_t n, int64_t x_row_stride,
+                         const int64_t *dst_row, int64_t cache_rows, uint32_t *codes, uint32_t *signs, float *norms,
+                         float *res_norms, float *dbg_rot, float *dbg_proj, tq::EncodeArgs *out) {
   if (cb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
   if (cb->device < 0) return fail(TQ_ERR_INVALID_ARG, "host-only codebook cannot encode");
   const int d = cb->host.d, m = cb->host.m;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "x_dtype must be TQ_F32 or TQ_BF16");
   if (n < 0) return fail(TQ_ERR_INVALID_ARG, "n < 0");
-  if (n == 0) return ok();
+  if (n == 0) return ok();   // nothing to launch
   if (x == nullptr || codes == nullptr || norms == nullptr) return fail(TQ_ERR_INVALID_ARG, "x, codes and norms are required");
   if (x_row_stride < d) return fail(TQ_ERR_INVALID_ARG, "x_row_stride (%lld) < head_dim", static_cast<long long>(x_row_stride));
   const size_t esize = (x_dtype == TQ_F32) ? 4 : 2;
@@ -280,12 +285,31 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *x, tq_dtype x_dtype, i
   a.qlut = dev_ptr<float4>(cb, cb->off_qcells);
   a.qscale = cb->qscale;
   a.qbias = cb->qbias;
+  *out = a;
+  return ok();
+}
+
+tq_status run_encode(const tq_codebook *cb, const tq::EncodeArgs &a, bool x_f32, void *stream) {
   DeviceGuard guard(cb->device);
   if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
-  hipError_t e = tq::launch_encode(a, cb->host.bits, m > 0, x_dtype == TQ_F32, cu_count(cb->device),
+  hipError_t e = tq::launch_encode(a, cb->host.bits, cb->host.m > 0, x_f32, cu_count(cb->device),
                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "encode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_encode_kv(const tq_codebook *cb, const void *x, tq_dtype x_dtype, int64_t n, int64_t x_row_stride,
+                       const int64_t *dst_row, int64_t cache_rows, uint32_t *codes, uint32_t *signs, float *norms,
+                       float *res_norms, float *dbg_rot, float *dbg_proj, void *stream) {
+  tq::EncodeArgs a{};
+  tq_status st = prepare_encode(cb, x, x_dtype, n, x_row_stride, dst_row, cache_rows, codes, signs, norms, res_norms,
+                                dbg_rot, dbg_proj, &a);
+  if (st != TQ_OK || n == 0) return st;
+  return run_encode(cb, a, x_dtype == TQ_F32, stream);
 }
 
 tq_status tq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t t_cap,
@@ -299,11 +323,15 @@ tq_status tq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_
   return ok();
 }
 
-tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
-                              const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
-                              int32_t n_q_heads, int32_t n_kv_heads, float softmax_scale, void *out,
-                              tq_dtype out_dtype, float *dbg_scores, void *workspace, size_t workspace_bytes,
-                              void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch arguments of a decode (no launch).
+tq_status prepare_decode(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
+                         const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
+                         int32_t n_q_heads, int32_t n_kv_heads, float softmax_scale, void *out, tq_dtype out_dtype,
+                         float *dbg_scores, void *workspace, size_t workspace_bytes, tq::DecodeArgs *out_args) {
   if (kcb == nullptr || vcb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
   if (kcb->device < 0 || vcb->device != kcb->device)
     return fail(TQ_ERR_INVALID_ARG, "codebooks must live on the same GPU device");
@@ -366,11 +394,65 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
   a.ws_part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
   a.chunk = plan.chunk;
   a.n_chunks = plan.n_chunks;
+  *out_args = a;
+  return ok();
+}
+
+tq_status run_decode(const tq_codebook *kcb, const tq::DecodeArgs &a, void *stream) {
   DeviceGuard guard(kcb->device);
   if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
   hipError_t e = tq::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
+                              const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
+                              int32_t n_q_heads, int32_t n_kv_heads, float softmax_scale, void *out,
+                              tq_dtype out_dtype, float *dbg_scores, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  tq::DecodeArgs a{};
+  const tq_status st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, softmax_scale,
+                                      out, out_dtype, dbg_scores, workspace, workspace_bytes, &a);
+  if (st != TQ_OK) return st;
+  return run_decode(kcb, a, stream);
+}
+
+tq_status tq_append_decode(const tq_codebook *kcb, const tq_codebook *vcb, const void *k_new, const void *v_new,
+                           tq_dtype kv_dtype, const void *q, tq_dtype q_dtype, const tq_cache *k, const tq_cache *v,
+                           int32_t *seq_len, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                           float softmax_scale, void *out, tq_dtype out_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  tq::DecodeArgs da{};
+  tq_status st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, softmax_scale, out,
+                                out_dtype, nullptr, workspace, workspace_bytes, &da);
+  if (st != TQ_OK) return st;
+  if (k_new == nullptr || v_new == nullptr) return fail(TQ_ERR_INVALID_ARG, "k_new and v_new are required");
+  const int64_t n = static_cast<int64_t>(batch) * n_kv_heads;
+  const int64_t rows = n * k->t_cap;
+  const int d = kcb->host.d;
+  tq::EncodeArgs ka{}, va{};
+  st = prepare_encode(kcb, k_new, kv_dtype, n, d, nullptr, rows, const_cast<uint32_t *>(k->codes),
+                      const_cast<uint32_t *>(k->signs), const_cast<float *>(k->norms), const_cast<float *>(k->res_norms),
+                      nullptr, nullptr, &ka);
+  if (st != TQ_OK) return st;
+  st = prepare_encode(vcb, v_new, kv_dtype, n, d, nullptr, rows, const_cast<uint32_t *>(v->codes), nullptr,
+                      const_cast<float *>(v->norms), nullptr, nullptr, nullptr, &va);
+  if (st != TQ_OK) return st;
+  for (tq::EncodeArgs *ea : {&ka, &va}) {
+    ea->append_len = seq_len;
+    ea->append_heads = n_kv_heads;
+    ea->t_cap = k->t_cap;
+  }
+  da.seq_add = 1;
+  da.seq_inc = seq_len;
+  if ((st = run_encode(kcb, ka, kv_dtype == TQ_F32, stream)) != TQ_OK) return st;
+  if ((st = run_encode(vcb, va, kv_dtype == TQ_F32, stream)) != TQ_OK) return st;
+  return run_decode(kcb, da, stream);
 }
 
 const char *tq_status_string(tq_status s) {

@@ -291,7 +291,7 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   const int row_id = b * a.n_kv_heads + hk;             // (b, kv head)
   const int group_id = row_id * a.n_chunks + chunk_id;  // this work-group
 
-  int T = a.seq_len[b];
+  int T = a.seq_len[b] + a.seq_add;
   T = T < 0 ? 0 : (T > a.t_cap ? static_cast<int>(a.t_cap) : T);
   const int t_begin = chunk_id * a.chunk;
   const int t_end = min(T, t_begin + a.chunk);
@@ -730,6 +730,12 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
     } else {
       static_cast<float *>(a.out)[o_idx] = r;
     }
+  }
+  // Append steps: the sequence has one more cached token (the main kernel,
+  // the only reader of seq_len, has completed).
+  if (a.seq_inc != nullptr && hq == 0 && tid == 0) {
+    const int32_t s = a.seq_inc[b];
+    if (s >= 0 && s < a.t_cap) a.seq_inc[b] = s + 1;
   }
 }
 

@@ -112,6 +112,17 @@ __device__ __forceinline__ void load_x(const EncodeArgs &a, int64_t tile, int j,
   }
 }
 
+// Cache row of input vector `vec` (-1: not written).
+__device__ __forceinline__ int64_t dest_row(const EncodeArgs &a, int64_t vec, bool valid) {
+  if (!valid) return -1;
+  if (a.dst_row != nullptr) return a.dst_row[vec];
+  if (a.append_len != nullptr) {
+    const int32_t t = a.append_len[vec / a.append_heads];
+    return (t >= 0 && t < a.t_cap) ? vec * a.t_cap + t : -1;
+  }
+  return vec;
+}
+
 template <int BITS, bool QJL, bool XF32, bool DBG>
 __global__ __launch_bounds__(EncGeom<QJL>::kThreads) void encode_kernel(EncodeArgs a) {
   constexpr int NT = kNT;
@@ -318,8 +329,7 @@ __global__ __launch_bounds__(EncGeom<QJL>::kThreads) void encode_kernel(EncodeAr
     // ---- emit codes, norms, residual norms
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      int64_t row = vec[nt];
-      if (a.dst_row != nullptr) row = valid[nt] ? a.dst_row[vec[nt]] : -1;
+      const int64_t row = dest_row(a, vec[nt], valid[nt]);
       const bool ok = valid[nt] && row >= 0 && row < a.cache_rows;
       if constexpr (QJL) {
         rr[nt] += __shfl_xor(rr[nt], 16);

@@ -29,6 +29,12 @@ struct EncodeArgs {
   int64_t n;
   const int64_t *dst_row;  // may be null
   int64_t cache_rows;
+  // Append mode (dst_row null, append_len set): vector i goes to row
+  // i * t_cap + append_len[i / append_heads], skipped when that position is
+  // outside [0, t_cap).
+  const int32_t *append_len;
+  int append_heads;
+  int64_t t_cap;
   uint32_t *codes;
   uint32_t *signs;
   float *norms;
@@ -89,6 +95,8 @@ struct DecodeArgs {
   const float *v_norms;
   int64_t t_cap;
   const int32_t *seq_len;
+  int seq_add;             // tokens attended: clamp(seq_len[b] + seq_add, 0, t_cap)
+  int32_t *seq_inc;        // if set: seq_len[b] += 1 after the step when 0 <= seq_len[b] < t_cap
   int batch, n_q_heads, n_kv_heads;
   int k_bits, v_bits, qjl_m;
   float scale;
