@@ -228,11 +228,40 @@ def main():
         },
         "wall_s_timed": round(wall, 4),
     }
+    line["attention_logits"] = logits_only(T, kcb, q, caches, seq, ws, n_vec * k_rec, B * Hq * S * 4, args, dev)
     if args.append_steps > 0:
         line["append_step_us"] = append_steps(wl, kcb, vcb, up, args.append_steps, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, qjl=bool(qjl_m))
     print(json.dumps(line), flush=True)
+
+
+def logits_only(T, kcb, q, caches, seq, ws, key_bytes, logit_bytes, args, dev):
+    """Scores-only launches (the key phase of the decode, every logit written)
+    over the same cold cache replicas, timed after the step loop: mean time per
+    launch and algorithmic bytes (key records read + fp32 logits written)."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    B, Hq = q.shape[0], q.shape[1]
+    logits = torch.empty(B, Hq, caches[0][0].t_cap, dtype=torch.float32, device=dev)
+    for s in range(args.warmup):
+        T.attention_logits(kcb, q, caches[s % len(caches)][0], seq, logits=logits, workspace=ws, stream=stream)
+    n = max(1, args.steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    # a launch takes less GPU time than its host-side call: a spin kernel
+    # first lets the host queue all n launches, which then run back to back
+    torch.cuda._sleep(50_000_000)
+    start.record(stream)
+    for s in range(n):
+        T.attention_logits(kcb, q, caches[s % len(caches)][0], seq, logits=logits, workspace=ws, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / n
+    gbps = (key_bytes + logit_bytes) / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "achieved": round(gbps, 1), "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": key_bytes + logit_bytes,
+            "key_record_bytes": key_bytes, "logit_bytes": logit_bytes}
 
 
 def append_steps(wl, kcb, vcb, up, steps, dev):

@@ -197,6 +197,32 @@ tq_status tq_append_decode(const tq_codebook *kcb, const tq_codebook *vcb, const
                            float softmax_scale, void *out, tq_dtype out_dtype, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* Scaled attention logits of every cached token, without the softmax and the
+ * value sum: the key phase of tq_decode_attention on its own [admirer.cn
+ * memory-wall article, section 2: the attention logits computed from the
+ * compressed key cache, the operation the pages time against a JAX baseline
+ * at each bit width; intelliparadigm "3-bit" article, section 2.1.2: inner
+ * products estimated from the codes and the QJL signs].
+ *   kcb           key codebook (its Pi, S, centroids), on a GPU device.
+ *   q             device [batch][n_q_heads][d] of q_dtype (contiguous).
+ *   k             host struct holding device pointers to the key cache.
+ *   seq_len       device int32[batch]: tokens per sequence, clamped to [0, t_cap].
+ *   n_q_heads     n_kv_heads times 1, 2, 4 or 8 (else TQ_ERR_UNSUPPORTED).
+ *   softmax_scale <= 0 selects 1/sqrt(d).
+ *   logits        device float[batch][n_q_heads][t_cap] (caller-owned):
+ *                 entry t < seq_len[b] gets l_t; the others are not written.
+ *   workspace     device scratch of at least tq_decode_workspace_bytes bytes for
+ *                 the same sizes, 256-byte aligned; calls that share it must not
+ *                 overlap in time.
+ * l_t = scale * nu_t * ( <Pi q, c_k[code_t]> + sqrt(pi/2)/m * gamma_t *
+ * <S Pi q, 2 z_t - 1> ), bit for bit the l_t that tq_decode_attention returns
+ * in dbg_scores for the same inputs.  Errors: TQ_ERR_INVALID_ARG for NULL or
+ * misaligned pointers, bad sizes or a short workspace; nothing is launched then. */
+tq_status tq_attention_logits(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, const tq_cache *k,
+                              const int32_t *seq_len, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                              float softmax_scale, float *logits, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /* Static name of a status code. */
 const char *tq_status_string(tq_status s);
 

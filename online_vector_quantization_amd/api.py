@@ -24,7 +24,7 @@ TQ_F32, TQ_BF16 = 0, 1
 EXPORTED = (
     "tq_codebook_build", "tq_codebook_free", "tq_codebook_info", "tq_codebook_export",
     "tq_codebook_export_f64", "tq_record_words", "tq_encode_kv", "tq_decode_workspace_bytes",
-    "tq_decode_attention", "tq_append_decode", "tq_status_string", "tq_last_error",
+    "tq_decode_attention", "tq_append_decode", "tq_attention_logits", "tq_status_string", "tq_last_error",
 )
 
 
@@ -64,6 +64,8 @@ def load_library() -> ctypes.CDLL:
                                         i32, i32, i32, f32, vp, i32, vp, vp, ctypes.c_size_t, vp]
     lib.tq_append_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache),
                                      vp, i32, i32, i32, f32, vp, i32, vp, ctypes.c_size_t, vp]
+    lib.tq_attention_logits.argtypes = [vp, vp, i32, ctypes.POINTER(TqCache), vp, i32, i32, i32, f32, vp, vp,
+                                        ctypes.c_size_t, vp]
     for name in EXPORTED:
         if name not in ("tq_status_string", "tq_last_error"):
             getattr(lib, name).restype = ctypes.c_int
@@ -287,6 +289,32 @@ def append_decode(kcb: Codebook, vcb: Codebook, k_new: torch.Tensor, v_new: torc
         ctypes.byref(ks), ctypes.byref(vs), _ptr(seq_len), B, Hq, Hkv, float(softmax_scale), _ptr(out),
         _dtype_code(out), _ptr(workspace), workspace.numel(), _stream_handle(stream, q.device)), "tq_append_decode")
     return out
+
+
+def attention_logits(kcb: Codebook, q: torch.Tensor, kcache: CompressedCache, seq_len: torch.Tensor,
+                     logits: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tq_attention_logits: the scaled logits of q [B, Hq, d] against every cached key ->
+    logits float32 [B, Hq, t_cap]; entries t >= seq_len[b] are not written (a new
+    logits tensor starts at -inf)."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, d] tensor")
+    B, Hq, d = q.shape
+    Hkv = kcache.codes.shape[1]
+    if seq_len.dtype != torch.int32 or seq_len.numel() != B or not seq_len.is_contiguous():
+        raise ValueError("seq_len must be a contiguous int32 tensor with B entries")
+    if logits is None:
+        logits = torch.full((B, Hq, kcache.t_cap), float("-inf"), dtype=torch.float32, device=q.device)
+    if logits.dtype != torch.float32 or tuple(logits.shape) != (B, Hq, kcache.t_cap) or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous float32 [B, Hq, t_cap] tensor")
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, kcache.t_cap, q.device)
+    _require_cuda(q, seq_len, logits, workspace, kcache.codes)
+    ks = kcache.as_struct()
+    _check(load_library().tq_attention_logits(
+        kcb.handle, _ptr(q), _dtype_code(q), ctypes.byref(ks), _ptr(seq_len), B, Hq, Hkv, float(softmax_scale),
+        _ptr(logits), _ptr(workspace), workspace.numel(), _stream_handle(stream, q.device)), "tq_attention_logits")
+    return logits
 
 
 def compressed_bytes_per_token(kcb: Codebook, vcb: Codebook) -> int:

@@ -327,36 +327,32 @@ tq_status tq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_
 
 namespace {
 
-// Validation and launch arguments of a decode (no launch).
-tq_status prepare_decode(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
-                         const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
-                         int32_t n_q_heads, int32_t n_kv_heads, float softmax_scale, void *out, tq_dtype out_dtype,
-                         float *dbg_scores, void *workspace, size_t workspace_bytes, tq::DecodeArgs *out_args) {
-  if (kcb == nullptr || vcb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
-  if (kcb->device < 0 || vcb->device != kcb->device)
-    return fail(TQ_ERR_INVALID_ARG, "codebooks must live on the same GPU device");
-  if (kcb->host.d != vcb->host.d) return fail(TQ_ERR_INVALID_ARG, "key and value head_dim differ");
-  if (vcb->host.m != 0) return fail(TQ_ERR_INVALID_ARG, "the value codebook must have qjl_dim 0");
-  if (q == nullptr || k == nullptr || v == nullptr || seq_len == nullptr || out == nullptr || workspace == nullptr)
+// Validation and launch arguments of the key side of a decode (the query, the
+// key cache, seq_len, the workspace and the scores output); no launch.
+tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, const tq_cache *k,
+                       const int32_t *seq_len, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                       float softmax_scale, float *scores, void *workspace, size_t workspace_bytes,
+                       tq::DecodeArgs *out_args) {
+  if (kcb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  if (kcb->device < 0) return fail(TQ_ERR_INVALID_ARG, "the codebook must live on a GPU device");
+  if (q == nullptr || k == nullptr || seq_len == nullptr || workspace == nullptr)
     return fail(TQ_ERR_INVALID_ARG, "NULL argument");
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad q_dtype");
-  if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad out_dtype");
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0)
     return fail(TQ_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d/%d)", batch, n_q_heads, n_kv_heads);
   const int g = n_q_heads / n_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8)
     return fail(TQ_ERR_UNSUPPORTED, "q heads per kv head must be 1, 2, 4 or 8 (got %d)", g);
-  if (k->t_cap < 1 || v->t_cap != k->t_cap) return fail(TQ_ERR_INVALID_ARG, "key/value t_cap must match and be >= 1");
+  if (k->t_cap < 1) return fail(TQ_ERR_INVALID_ARG, "t_cap must be >= 1");
   if (k->t_cap > (int64_t{1} << 30)) return fail(TQ_ERR_UNSUPPORTED, "t_cap above 2^30");
 
   const int m = kcb->host.m;
-  if (k->codes == nullptr || k->norms == nullptr || v->codes == nullptr || v->norms == nullptr)
-    return fail(TQ_ERR_INVALID_ARG, "cache codes/norms are required");
+  if (k->codes == nullptr || k->norms == nullptr) return fail(TQ_ERR_INVALID_ARG, "cache codes/norms are required");
   if ((m > 0) != (k->signs != nullptr) || (m > 0) != (k->res_norms != nullptr))
     return fail(TQ_ERR_INVALID_ARG, "key signs/res_norms must be given iff the key codebook has qjl_dim > 0");
-  if (!aligned(k->codes, 16) || !aligned(v->codes, 16) || (k->signs && !aligned(k->signs, 16)) ||
-      !aligned(k->norms, 4) || !aligned(v->norms, 4) || !aligned(q, 4) || !aligned(out, 4) || !aligned(workspace, 256) ||
-      !aligned(seq_len, 4) || (dbg_scores && !aligned(dbg_scores, 4)))
+  if (!aligned(k->codes, 16) || (k->signs && !aligned(k->signs, 16)) || !aligned(k->norms, 4) ||
+      (k->res_norms && !aligned(k->res_norms, 4)) || !aligned(q, 4) || !aligned(workspace, 256) ||
+      !aligned(seq_len, 4) || (scores && !aligned(scores, 4)))
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer");
   const tq::DecodePlan plan = tq::plan_decode(batch, n_q_heads, n_kv_heads, k->t_cap);
   if (workspace_bytes < plan.total_bytes)
@@ -368,32 +364,57 @@ tq_status prepare_decode(const tq_codebook *kcb, const tq_codebook *vcb, const v
   a.k_signs = k->signs;
   a.k_norms = k->norms;
   a.k_res = k->res_norms;
-  a.v_codes = v->codes;
-  a.v_norms = v->norms;
   a.t_cap = k->t_cap;
   a.seq_len = seq_len;
   a.batch = batch;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = n_kv_heads;
   a.k_bits = kcb->host.bits;
-  a.v_bits = vcb->host.bits;
   a.qjl_m = m;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(kcb->host.d));
   a.qjl_coef = m > 0 ? static_cast<float>(std::sqrt(3.14159265358979323846 / 2.0) / m) : 0.f;
-  a.out = out;
-  a.out_bf16 = (out_dtype == TQ_BF16);
-  a.dbg_scores = dbg_scores;
+  a.scores = scores;
   a.rot_k_t = dev_ptr<float>(kcb, kcb->off_rot_t_f32);
   a.qjl_rot_t = m > 0 ? dev_ptr<float>(kcb, kcb->off_qjl_rot_t_f32) : nullptr;
-  a.rot_v = dev_ptr<float>(vcb, vcb->off_rot_f32);
   a.k_lut = dev_ptr<float>(kcb, kcb->off_key_lut);
-  a.v_lut = dev_ptr<float>(vcb, vcb->off_pair_lut);
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   a.ws_qslot = reinterpret_cast<float *>(ws + plan.off_qslot);
   a.ws_part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
   a.ws_part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
   a.chunk = plan.chunk;
   a.n_chunks = plan.n_chunks;
+  *out_args = a;
+  return ok();
+}
+
+// Validation and launch arguments of a decode (no launch): the key side, then
+// the value cache, its codebook and the output.
+tq_status prepare_decode(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
+                         const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
+                         int32_t n_q_heads, int32_t n_kv_heads, float softmax_scale, void *out, tq_dtype out_dtype,
+                         float *dbg_scores, void *workspace, size_t workspace_bytes, tq::DecodeArgs *out_args) {
+  if (kcb == nullptr || vcb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  if (kcb->device < 0 || vcb->device != kcb->device)
+    return fail(TQ_ERR_INVALID_ARG, "codebooks must live on the same GPU device");
+  if (kcb->host.d != vcb->host.d) return fail(TQ_ERR_INVALID_ARG, "key and value head_dim differ");
+  if (vcb->host.m != 0) return fail(TQ_ERR_INVALID_ARG, "the value codebook must have qjl_dim 0");
+  if (v == nullptr || out == nullptr) return fail(TQ_ERR_INVALID_ARG, "NULL argument");
+  if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad out_dtype");
+  tq::DecodeArgs a{};
+  const tq_status st = prepare_keys(kcb, q, q_dtype, k, seq_len, batch, n_q_heads, n_kv_heads, softmax_scale,
+                                    dbg_scores, workspace, workspace_bytes, &a);
+  if (st != TQ_OK) return st;
+  if (v->t_cap != k->t_cap) return fail(TQ_ERR_INVALID_ARG, "key/value t_cap must match");
+  if (v->codes == nullptr || v->norms == nullptr) return fail(TQ_ERR_INVALID_ARG, "cache codes/norms are required");
+  if (!aligned(v->codes, 16) || !aligned(v->norms, 4) || !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer");
+  a.v_codes = v->codes;
+  a.v_norms = v->norms;
+  a.v_bits = vcb->host.bits;
+  a.out = out;
+  a.out_bf16 = (out_dtype == TQ_BF16);
+  a.rot_v = dev_ptr<float>(vcb, vcb->off_rot_f32);
+  a.v_lut = dev_ptr<float>(vcb, vcb->off_pair_lut);
   *out_args = a;
   return ok();
 }
@@ -453,6 +474,22 @@ tq_status tq_append_decode(const tq_codebook *kcb, const tq_codebook *vcb, const
   if ((st = run_encode(kcb, ka, kv_dtype == TQ_F32, stream)) != TQ_OK) return st;
   if ((st = run_encode(vcb, va, kv_dtype == TQ_F32, stream)) != TQ_OK) return st;
   return run_decode(kcb, da, stream);
+}
+
+tq_status tq_attention_logits(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, const tq_cache *k,
+                              const int32_t *seq_len, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                              float softmax_scale, float *logits, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  if (logits == nullptr) return fail(TQ_ERR_INVALID_ARG, "logits is NULL");
+  tq::DecodeArgs a{};
+  const tq_status st = prepare_keys(kcb, q, q_dtype, k, seq_len, batch, n_q_heads, n_kv_heads, softmax_scale, logits,
+                                    workspace, workspace_bytes, &a);
+  if (st != TQ_OK) return st;
+  DeviceGuard guard(kcb->device);
+  if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
+  const hipError_t e = tq::launch_logits(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "logits launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 const char *tq_status_string(tq_status s) {

@@ -260,7 +260,9 @@ template <int KB, int G> struct KeyTab {
 // same softmax, with far fewer wave reductions and rescales.
 constexpr float kLazy = 8.f;
 
-template <int KB, bool QJL, int G>
+// SC (scores only): the prologue and key phase alone; every l_t of the chunk
+// goes to a.scores and the kernel ends after its last tile.
+template <int KB, bool QJL, int G, bool SC>
 __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a) {
   using KL = KeyLut<KB>;
   constexpr int kWaves = Geom<G>::kWaves;
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   constexpr int kPass = 64 * kWaves;
   constexpr int KW = D * KB / 32;   // key code words per token
   __shared__ float s_kdeq[KL::kEntries * KL::kCoords];
-  __shared__ float2 s_vdeq[256];
+  __shared__ float2 s_vdeq[SC ? 1 : 256];
   // QJL sign table, entry (pos, nib, h) = sum_{k<4} s_h[4 pos + k] * (bit k of nib ? +1 : -1)
   __shared__ float s_slut[QJL ? kSignLut * G : 1];
   using KT = KeyTab<KB, G>;
@@ -319,9 +321,11 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
     const uint4 *kl = reinterpret_cast<const uint4 *>(a.k_lut);
     uint4 *kd = reinterpret_cast<uint4 *>(s_kdeq);
     for (int e = tid; e < KL::kEntries * KL::kCoords / 4; e += kThreads) kd[e] = kl[e];
-    const uint4 *vl = reinterpret_cast<const uint4 *>(a.v_lut);
-    uint4 *vd = reinterpret_cast<uint4 *>(s_vdeq);
-    for (int e = tid; e < (1 << (2 * VB)) / 2; e += kThreads) vd[e] = vl[e];
+    if constexpr (!SC) {
+      const uint4 *vl = reinterpret_cast<const uint4 *>(a.v_lut);
+      uint4 *vd = reinterpret_cast<uint4 *>(s_vdeq);
+      for (int e = tid; e < (1 << (2 * VB)) / 2; e += kThreads) vd[e] = vl[e];
+    }
   }
   __syncthreads();
   // The first tile's records are requested now: after the prologue's own reads
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   ValRegs vcur{};
   if (tb0 < t_end) {
     cur = load_keys<KW, QJL>(a, row_of(tb0));
-    vcur = load_values(a, row0 + tb0, t_end - tb0, row_of(tb0), VW, lane);
+    if constexpr (!SC) vcur = load_values(a, row0 + tb0, t_end - tb0, row_of(tb0), VW, lane);
   }
   {
     float aq[G], as[G];
@@ -424,7 +428,8 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   for (int tb = tb0; tb < t_end; tb += kPass) {
     const int t = tb + lane;
     const bool valid = t < t_end;
-    if (tb != tb0) vcur = load_values(a, row0 + tb, t_end - tb, row_of(tb), VW, lane);
+    if constexpr (!SC)
+      if (tb != tb0) vcur = load_values(a, row0 + tb, t_end - tb, row_of(tb), VW, lane);
     KeyRegs<KW> nxt{};
     if (tb + kPass < t_end) nxt = load_keys<KW, QJL>(a, row_of(tb + kPass));
     float l[G];
@@ -527,9 +532,13 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         l[h] = valid ? a.scale * nu * dot[h] : -INFINITY;
-        if (a.dbg_scores != nullptr && valid)
-          a.dbg_scores[(static_cast<int64_t>(b) * a.n_q_heads + hq0 + h) * a.t_cap + t] = l[h];
+        if ((SC || a.scores != nullptr) && valid)
+          a.scores[(static_cast<int64_t>(b) * a.n_q_heads + hq0 + h) * a.t_cap + t] = l[h];
       }
+    }
+    if constexpr (SC) {
+      cur = nxt;
+      continue;
     }
     // ---- online softmax (lazy running max)
     bool grow = false;
@@ -591,6 +600,8 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     cur = nxt;
   }
+
+  if constexpr (SC) return;   // uniform: no barrier follows for any thread
 
   // ------------------------------------------------------------ 2. merge waves
   float l_wave[G];
@@ -739,11 +750,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
   }
 }
 
-template <int KB, bool QJL>
+template <int KB, bool QJL, bool SC>
 hipError_t launch_g(const DecodeArgs &a, int g, dim3 grid, hipStream_t stream) {
   switch (g) {
 #define TQ_G(GG) \
-  case GG: hipLaunchKernelGGL((decode_kernel<KB, QJL, GG>), grid, dim3(Geom<GG>::kThreads), 0, stream, a); break;
+  case GG: hipLaunchKernelGGL((decode_kernel<KB, QJL, GG, SC>), grid, dim3(Geom<GG>::kThreads), 0, stream, a); break;
     TQ_G(1) TQ_G(2) TQ_G(4) TQ_G(8)
 #undef TQ_G
     default: return hipErrorInvalidValue;
@@ -751,9 +762,23 @@ hipError_t launch_g(const DecodeArgs &a, int g, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int KB>
+template <int KB, bool SC>
 hipError_t launch_q(const DecodeArgs &a, int g, dim3 grid, hipStream_t stream) {
-  return a.qjl_m > 0 ? launch_g<KB, true>(a, g, grid, stream) : launch_g<KB, false>(a, g, grid, stream);
+  return a.qjl_m > 0 ? launch_g<KB, true, SC>(a, g, grid, stream) : launch_g<KB, false, SC>(a, g, grid, stream);
+}
+
+template <bool SC>
+hipError_t launch_main(const DecodeArgs &a, hipStream_t stream) {
+  const int g = a.n_q_heads / a.n_kv_heads;
+  if (a.n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
+  const dim3 grid(a.n_chunks, a.n_kv_heads, a.batch);
+  switch (a.k_bits) {
+    case 1: return launch_q<1, SC>(a, g, grid, stream);
+    case 2: return launch_q<2, SC>(a, g, grid, stream);
+    case 3: return launch_q<3, SC>(a, g, grid, stream);
+    case 4: return launch_q<4, SC>(a, g, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -783,20 +808,15 @@ DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int64_t t_cap) 
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  const int g = a.n_q_heads / a.n_kv_heads;
-  if (a.n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
-  const dim3 grid(a.n_chunks, a.n_kv_heads, a.batch);
-  hipError_t e;
-  switch (a.k_bits) {
-    case 1: e = launch_q<1>(a, g, grid, stream); break;
-    case 2: e = launch_q<2>(a, g, grid, stream); break;
-    case 3: e = launch_q<3>(a, g, grid, stream); break;
-    case 4: e = launch_q<4>(a, g, grid, stream); break;
-    default: return hipErrorInvalidValue;
-  }
+  const hipError_t e = launch_main<false>(a, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(kCombThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_logits(const DecodeArgs &a, hipStream_t stream) {
+  if (a.scores == nullptr) return hipErrorInvalidValue;
+  return launch_main<true>(a, stream);
 }
 
 }  // namespace tq

@@ -103,7 +103,7 @@ struct DecodeArgs {
   float qjl_coef;          // sqrt(pi/2)/m
   void *out;
   int out_bf16;
-  float *dbg_scores;
+  float *scores;           // float[B][Hq][t_cap] scaled logits of t < T; optional for attention, the output of the logits-only kernel
   const float *rot_k_t;    // Pi_k^T row-major (d x d): entry [i][j] = Pi_k[j][i]
   const float *qjl_rot_t;  // (S Pi_k)^T row-major (d x m): s = S Pi_k q in one product
   const float *rot_v;      // Pi_v row-major (d x d)
@@ -116,5 +116,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// Scores only: the decode's key phase, writing every l_t to a.scores (no value
+// phase, no combine; the value fields are not read).
+hipError_t launch_logits(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace tq

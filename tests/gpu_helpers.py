@@ -151,3 +151,43 @@ def check_decode(kcb, vcb, q_dev, kc, vc, seq_len, kbits, vbits, m, score_tol=1e
     err = np.abs(o32 - ref_out).max()
     assert err <= out_tol, f"output max-abs error {err:.3e}"
     return err
+
+
+def oracle_logits(q_host, kc_host, seq_c, kb, g, scale=None):
+    """Oracle scaled logits [B, Hq, t_cap] (NaN past seq_len): decode_scores of
+    every (b, q head) over its kv head's first seq_len[b] cached keys."""
+    B, Hq, d = q_host.shape
+    t_cap = kc_host["norms"].shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    m = 0 if kb["S"] is None else kb["S"].shape[0]
+    out = np.full((B, Hq, t_cap), np.nan)
+    for b in range(B):
+        Tb = seq_c[b]
+        if Tb == 0:
+            continue
+        for hk in range(Hq // g):
+            idx = O.unpack_bits(kc_host["codes"][b, hk, :Tb], d, kb["bits"])
+            z = O.unpack_bits(kc_host["signs"][b, hk, :Tb], m, 1).astype(bool) if m else None
+            gam = kc_host["res_norms"][b, hk, :Tb] if m else None
+            for j in range(g):
+                out[b, hk * g + j, :Tb] = O.decode_scores(q_host[b, hk * g + j], kb["Pi"], kb["centroids"], kb["S"],
+                                                          idx, kc_host["norms"][b, hk, :Tb], gam, z, scale)
+    return out
+
+
+def check_logits(got: np.ndarray, ref: np.ndarray, seq_c, tol=1e-4):
+    """Per (b, q head): max |got - ref| <= tol * max |ref| over t < seq_len;
+    entries past seq_len keep the caller's NaN sentinel."""
+    B, Hq, _ = ref.shape
+    worst = 0.0
+    for b in range(B):
+        Tb = seq_c[b]
+        for h in range(Hq):
+            assert np.all(np.isnan(got[b, h, Tb:])), f"logits written past seq_len (b={b} h={h})"
+            if Tb == 0:
+                continue
+            r = ref[b, h, :Tb]
+            err = np.abs(got[b, h, :Tb].astype(np.float64) - r).max() / np.abs(r).max()
+            assert err <= tol, f"logits b={b} h={h}: relative error {err:.3e}"
+            worst = max(worst, err)
+    return worst

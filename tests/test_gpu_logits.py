@@ -1,0 +1,119 @@
+"""tq_attention_logits: the scaled logits of every cached key, without the
+softmax and the value sum.
+
+* Oracle parity (decode_scores per (b, q head)) at every key width, with and
+  without the QJL sign bits, at g = 1, 2, 4, 8, over caches of several
+  work-group chunks with ragged, empty and full sequences; entries past
+  seq_len are not written.
+* Bit-equal to the l_t that tq_decode_attention reports for the same inputs.
+* Full sizes: the Llama-3-8B-shaped layer (32768 tokens, 32 q heads) and the
+  batched workload (16 x 8 x 8192, b = 2), every logit checked.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from online_vector_quantization_amd import synth  # noqa: E402
+
+import gpu_helpers as H  # noqa: E402
+import online_vector_quantization_amd as T  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; torch sees no GPU")
+    T.load_library()
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _nan_logits(B, Hq, t_cap):
+    return torch.full((B, Hq, t_cap), float("nan"), dtype=torch.float32, device=H.DEV)
+
+
+@pytest.mark.parametrize("kbits,m,g", [(1, 128, 4), (2, 128, 8), (3, 128, 2), (4, 128, 1),
+                                       (1, 0, 2), (2, 0, 4), (3, 0, 8), (4, 0, 1)])
+def test_logits_parity(kbits, m, g):
+    B, Hkv, t_cap = 4, 2, 1300
+    lens = [1300, 0, 777, 5]
+    Hq = Hkv * g
+    rng = np.random.default_rng(100 * kbits + 10 * g + (m > 0))
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap, lognormal_sigma=0.5))
+    v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap, lognormal_sigma=0.5))
+    q = H.to_device(synth.bf16_bits(rng.standard_normal((B, Hq, 128)).astype(np.float32)), "bf16")
+    kcb, vcb = H.gpu_book(kbits, m), H.gpu_book(2, 0)
+    kc, vc = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, t_cap, t_cap)
+    sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+    _log(f"logits kbits={kbits} m={m} g={g} lens={lens}")
+    got = T.attention_logits(kcb, q, kc, sl, logits=_nan_logits(B, Hq, t_cap))
+    dbg = _nan_logits(B, Hq, t_cap)
+    T.decode_attention(kcb, vcb, q, kc, vc, sl, dbg_scores=dbg)
+    torch.cuda.synchronize()
+    g_np = got.cpu().numpy()
+    # the decode's own logits, bit for bit (NaN sentinels included)
+    np.testing.assert_array_equal(g_np.view(np.uint32), dbg.cpu().numpy().view(np.uint32))
+    ref = H.oracle_logits(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), lens,
+                          H.oracle_book(kbits, m), g)
+    H.check_logits(g_np, ref, lens)
+
+
+def test_logits_scale_and_seq_clamp():
+    """softmax_scale scales every logit; seq_len beyond t_cap is clamped and
+    a negative one reads as empty."""
+    B, Hkv, g, t_cap = 3, 1, 4, 700
+    rng = np.random.default_rng(9)
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap))
+    q = H.to_device(synth.bf16_bits(rng.standard_normal((B, Hkv * g, 128)).astype(np.float32)), "bf16")
+    kcb = H.gpu_book(2, 128)
+    kc = T.CompressedCache.allocate(kcb, B, Hkv, t_cap)
+    T.encode_into_cache(kcb, H.to_device(k.reshape(-1, 128), "bf16"), kc)
+    sl = torch.tensor([10_000, -3, 333], dtype=torch.int32, device=H.DEV)
+    got = T.attention_logits(kcb, q, kc, sl, logits=_nan_logits(B, Hkv * g, t_cap), softmax_scale=0.5)
+    torch.cuda.synchronize()
+    seq_c = [t_cap, 0, 333]
+    ref = H.oracle_logits(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), seq_c,
+                          H.oracle_book(2, 128), g, scale=0.5)
+    H.check_logits(got.cpu().numpy(), ref, seq_c)
+
+
+def test_logits_llama8b_full():
+    wl = synth.llama8b()
+    S = wl.seq_len
+    _log(f"{wl.name}: logits of all {S} tokens x 32 q heads")
+    kcb = H.gpu_book(2, 128)
+    kc = T.CompressedCache.allocate(kcb, 1, 8, S)
+    T.encode_into_cache(kcb, H.to_device(wl.k.reshape(-1, 128), "bf16"), kc)
+    q = H.to_device(wl.q, "bf16")
+    sl = torch.tensor([S], dtype=torch.int32, device=H.DEV)
+    ws = T.alloc_workspace(1, 32, 8, S, H.DEV)
+    got = T.attention_logits(kcb, q, kc, sl, logits=_nan_logits(1, 32, S), workspace=ws)
+    torch.cuda.synchronize()
+    ref = H.oracle_logits(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), [S],
+                          H.oracle_book(2, 128), 4)
+    worst = H.check_logits(got.cpu().numpy(), ref, [S])
+    _log(f"  worst relative error {worst:.2e}")
+
+
+def test_logits_batched_full():
+    wl = synth.batched(2)
+    B, Hkv, S = wl.batch, wl.n_kv_heads, wl.seq_len
+    _log(f"{wl.name}: logits of {B} x {Hkv} x {S} keys, 32 q heads")
+    kcb = H.gpu_book(1, 128)
+    kc = T.CompressedCache.allocate(kcb, B, Hkv, S)
+    T.encode_into_cache(kcb, H.to_device(wl.k.reshape(-1, 128), "bf16"), kc)
+    q = H.to_device(wl.q, "bf16")
+    lens = [S - 37 * b for b in range(B)]
+    sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+    got = T.attention_logits(kcb, q, kc, sl, logits=_nan_logits(B, 32, S))
+    torch.cuda.synchronize()
+    ref = H.oracle_logits(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), lens,
+                          H.oracle_book(1, 128), 4)
+    worst = H.check_logits(got.cpu().numpy(), ref, lens)
+    _log(f"  worst relative error {worst:.2e}")

@@ -107,6 +107,12 @@ def test_host_only_handle_refuses_encode_and_decode():
     s = lib.tq_decode_attention(cb.handle, cb.handle, buf, 1, ctypes.byref(cache), ctypes.byref(cache), buf,
                                 1, 1, 1, 0.0, buf, 0, None, buf, 4096, None)
     assert s == T.api.TQ_ERR_INVALID_ARG
+    s = lib.tq_attention_logits(cb.handle, buf, 1, ctypes.byref(cache), buf, 1, 1, 1, 0.0, buf, buf, 4096, None)
+    assert s == T.api.TQ_ERR_INVALID_ARG
+    assert b"GPU device" in lib.tq_last_error()
+    s = lib.tq_attention_logits(cb.handle, buf, 1, ctypes.byref(cache), buf, 1, 1, 1, 0.0, None, buf, 4096, None)
+    assert s == T.api.TQ_ERR_INVALID_ARG
+    assert b"logits is NULL" in lib.tq_last_error()
 
 
 def test_encode_zero_rows_is_a_noop_and_bad_dtype_rejected():
