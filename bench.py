@@ -56,6 +56,8 @@ def parse():
                          "separate calls, tq_append_decode, and one captured step replayed as a graph")
     ap.add_argument("--key-mode", default="qjl", choices=["qjl", "mse"],
                     help="keys as (b-1)-bit codes + 1-bit QJL (default) or b-bit MSE-only codes")
+    ap.add_argument("--chunk", type=int, default=16, metavar="N",
+                    help="also time causal attention of N new queries per head over the full cache (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle step until this much CPU time has run")
@@ -229,6 +231,8 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     line["attention_logits"] = logits_only(T, kcb, q, caches, seq, ws, n_vec * k_rec, B * Hq * S * 4, args, dev)
+    if args.chunk > 0:
+        line["chunk_attention"] = chunk_only(T, kcb, vcb, caches, S, Hq, args, dev)
     if args.append_steps > 0:
         line["append_step_us"] = append_steps(wl, kcb, vcb, up, args.append_steps, dev)
     if not args.no_cpu_baseline:
@@ -262,6 +266,39 @@ def logits_only(T, kcb, q, caches, seq, ws, key_bytes, logit_bytes, args, dev):
     return {"us": round(us, 2), "achieved": round(gbps, 1), "unit": "GB/s", "peak": HBM_PEAK_GBPS,
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": key_bytes + logit_bytes,
             "key_record_bytes": key_bytes, "logit_bytes": logit_bytes}
+
+
+def chunk_only(T, kcb, vcb, caches, S, Hq, args, dev):
+    """Causal attention of args.chunk new queries per (b, q head), the last
+    positions of a full cache, over the same cold cache replicas: mean time per
+    launch pair and the cache bytes per launch (each query block re-reads them)."""
+    import torch
+    n_new = args.chunk
+    stream = torch.cuda.current_stream(dev)
+    kc0, vc0 = caches[0]
+    B = kc0.codes.shape[0]
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    q = torch.randn(B, Hq, n_new, 128, generator=g, device=dev).to(torch.bfloat16)
+    seq = torch.full((B,), S, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, n_new, 128, dtype=torch.bfloat16, device=dev)
+    ws = T.alloc_workspace(B * n_new, Hq, kc0.codes.shape[1], kc0.t_cap, dev)
+    run = lambda s: T.chunk_attention(kcb, vcb, q, caches[s % len(caches)][0], caches[s % len(caches)][1], seq,
+                                      out=out, workspace=ws, stream=stream)
+    for s in range(args.warmup):
+        run(s)
+    n = max(1, args.steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(n):
+        run(s)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / n
+    cache_bytes = B * kc0.codes.shape[1] * S * T.compressed_bytes_per_token(kcb, vcb)
+    return {"n_new": n_new, "us": round(us, 2), "queries_per_s": round(B * Hq * n_new / (us * 1e-6), 1),
+            "cache_bytes": cache_bytes, "cache_gbps_per_query_block": round(cache_bytes * n_new / (us * 1e-6) / 1e9, 1)}
 
 
 def append_steps(wl, kcb, vcb, up, steps, dev):

@@ -172,6 +172,34 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
                               tq_dtype out_dtype, float *dbg_scores, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* Attention of a chunk of n_new new tokens' queries over the compressed cache
+ * (chunked prefill, or several decode tokens verified at once), each query
+ * causal: query j of sequence b sits at position p = seq_len[b] - n_new + j
+ * and attends over cached positions 0 .. p [admirer.cn memory-wall article,
+ * section 1: every new token attends over the keys and values of all tokens
+ * before it; section 2: the attention runs on the compressed cache].  The new
+ * tokens' own K and V must already be in the cache (tq_encode_kv).
+ *   q             device [batch][n_q_heads][n_new][d] of q_dtype (contiguous).
+ *   seq_len       device int32[batch]: cached tokens including the n_new new
+ *                 ones; query j attends over clamp(seq_len[b] - n_new + j + 1,
+ *                 0, t_cap) tokens (zero output when that is 0).
+ *   n_new         >= 1, with n_new * n_kv_heads <= 65535, batch <= 65535 and
+ *                 batch * n_q_heads * n_new <= 2^24 (else TQ_ERR_INVALID_ARG).
+ *   out           device [batch][n_q_heads][n_new][d] of out_dtype.
+ *   workspace     at least tq_decode_workspace_bytes(batch * n_new, n_q_heads,
+ *                 n_kv_heads, t_cap) bytes, 256-byte aligned; calls that share
+ *                 it must not overlap in time.
+ * Other arguments as in tq_decode_attention.  With n_new = 1 the result equals
+ * tq_decode_attention bit for bit.  Query j's result equals tq_decode_attention
+ * of that query alone with seq_len[b] - n_new + j + 1 tokens up to the order of
+ * the split sums: the token chunks are sized for the whole launch, so they
+ * match (and the results are bitwise equal) only when both launches pick the
+ * same chunk length. */
+tq_status tq_chunk_attention(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
+                             const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, int32_t n_new, float softmax_scale, void *out,
+                             tq_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
 /* One step of a decode loop, enqueued on `stream` with no host synchronization
  * (so a caller can capture it in a graph and replay it): the new key and value
  * of every (b, kv head) are appended to the caches, the queries attend over

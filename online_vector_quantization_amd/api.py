@@ -24,7 +24,7 @@ TQ_F32, TQ_BF16 = 0, 1
 EXPORTED = (
     "tq_codebook_build", "tq_codebook_free", "tq_codebook_info", "tq_codebook_export",
     "tq_codebook_export_f64", "tq_record_words", "tq_encode_kv", "tq_decode_workspace_bytes",
-    "tq_decode_attention", "tq_append_decode", "tq_attention_logits", "tq_status_string", "tq_last_error",
+    "tq_decode_attention", "tq_append_decode", "tq_attention_logits", "tq_chunk_attention", "tq_status_string", "tq_last_error",
 )
 
 
@@ -64,6 +64,8 @@ def load_library() -> ctypes.CDLL:
                                         i32, i32, i32, f32, vp, i32, vp, vp, ctypes.c_size_t, vp]
     lib.tq_append_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache),
                                      vp, i32, i32, i32, f32, vp, i32, vp, ctypes.c_size_t, vp]
+    lib.tq_chunk_attention.argtypes = [vp, vp, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache), vp,
+                                       i32, i32, i32, i32, f32, vp, i32, vp, ctypes.c_size_t, vp]
     lib.tq_attention_logits.argtypes = [vp, vp, i32, ctypes.POINTER(TqCache), vp, i32, i32, i32, f32, vp, vp,
                                         ctypes.c_size_t, vp]
     for name in EXPORTED:
@@ -258,6 +260,31 @@ def decode_attention(kcb: Codebook, vcb: Codebook, q: torch.Tensor, kcache: Comp
         kcb.handle, vcb.handle, _ptr(q), _dtype_code(q), ctypes.byref(ks), ctypes.byref(vs), _ptr(seq_len),
         B, Hq, Hkv, float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(dbg_scores), _ptr(workspace),
         workspace.numel(), _stream_handle(stream, q.device)), "tq_decode_attention")
+    return out
+
+
+def chunk_attention(kcb: Codebook, vcb: Codebook, q: torch.Tensor, kcache: CompressedCache,
+                    vcache: CompressedCache, seq_len: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    softmax_scale: float = 0.0, out_dtype=torch.float32, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """tq_chunk_attention: q [B, Hq, n_new, d], query j at position seq_len[b] - n_new + j attending
+    causally over the compressed caches -> out [B, Hq, n_new, d]."""
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, n_new, d] tensor")
+    B, Hq, n_new, d = q.shape
+    Hkv = kcache.codes.shape[1]
+    if seq_len.dtype != torch.int32 or seq_len.numel() != B or not seq_len.is_contiguous():
+        raise ValueError("seq_len must be a contiguous int32 tensor with B entries")
+    if out is None:
+        out = torch.empty(B, Hq, n_new, d, dtype=out_dtype, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B * n_new, Hq, Hkv, kcache.t_cap, q.device)
+    _require_cuda(q, seq_len, out, workspace, kcache.codes, vcache.codes)
+    ks, vs = kcache.as_struct(), vcache.as_struct()
+    _check(load_library().tq_chunk_attention(
+        kcb.handle, vcb.handle, _ptr(q), _dtype_code(q), ctypes.byref(ks), ctypes.byref(vs), _ptr(seq_len),
+        B, Hq, Hkv, n_new, float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(workspace), workspace.numel(),
+        _stream_handle(stream, q.device)), "tq_chunk_attention")
     return out
 
 

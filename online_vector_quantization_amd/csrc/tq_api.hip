@@ -330,7 +330,7 @@ namespace {
 // Validation and launch arguments of the key side of a decode (the query, the
 // key cache, seq_len, the workspace and the scores output); no launch.
 tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, const tq_cache *k,
-                       const int32_t *seq_len, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                       const int32_t *seq_len, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t n_new,
                        float softmax_scale, float *scores, void *workspace, size_t workspace_bytes,
                        tq::DecodeArgs *out_args) {
   if (kcb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
@@ -343,6 +343,11 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
   const int g = n_q_heads / n_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8)
     return fail(TQ_ERR_UNSUPPORTED, "q heads per kv head must be 1, 2, 4 or 8 (got %d)", g);
+  // grid limits: y = n_kv_heads * n_new, z = batch; the combine launches batch * n_q_heads * n_new groups
+  if (n_new < 1 || batch > 65535 || static_cast<int64_t>(n_new) * n_kv_heads > 65535 ||
+      static_cast<int64_t>(batch) * n_q_heads * n_new > (int64_t{1} << 24))
+    return fail(TQ_ERR_INVALID_ARG, "bad sizes (batch %d, n_new %d, heads %d/%d): need batch <= 65535, "
+                "n_new * n_kv_heads <= 65535, batch * n_q_heads * n_new <= 2^24", batch, n_new, n_q_heads, n_kv_heads);
   if (k->t_cap < 1) return fail(TQ_ERR_INVALID_ARG, "t_cap must be >= 1");
   if (k->t_cap > (int64_t{1} << 30)) return fail(TQ_ERR_UNSUPPORTED, "t_cap above 2^30");
 
@@ -354,7 +359,7 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
       (k->res_norms && !aligned(k->res_norms, 4)) || !aligned(q, 4) || !aligned(workspace, 256) ||
       !aligned(seq_len, 4) || (scores && !aligned(scores, 4)))
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer");
-  const tq::DecodePlan plan = tq::plan_decode(batch, n_q_heads, n_kv_heads, k->t_cap);
+  const tq::DecodePlan plan = tq::plan_decode(batch * n_new, n_q_heads, n_kv_heads, k->t_cap);
   if (workspace_bytes < plan.total_bytes)
     return fail(TQ_ERR_INVALID_ARG, "workspace too small (%zu < %zu)", workspace_bytes, plan.total_bytes);
   tq::DecodeArgs a{};
@@ -369,6 +374,7 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
   a.batch = batch;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = n_kv_heads;
+  a.n_new = n_new;
   a.k_bits = kcb->host.bits;
   a.qjl_m = m;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(kcb->host.d));
@@ -391,8 +397,9 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
 // the value cache, its codebook and the output.
 tq_status prepare_decode(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
                          const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
-                         int32_t n_q_heads, int32_t n_kv_heads, float softmax_scale, void *out, tq_dtype out_dtype,
-                         float *dbg_scores, void *workspace, size_t workspace_bytes, tq::DecodeArgs *out_args) {
+                         int32_t n_q_heads, int32_t n_kv_heads, int32_t n_new, float softmax_scale, void *out,
+                         tq_dtype out_dtype, float *dbg_scores, void *workspace, size_t workspace_bytes,
+                         tq::DecodeArgs *out_args) {
   if (kcb == nullptr || vcb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
   if (kcb->device < 0 || vcb->device != kcb->device)
     return fail(TQ_ERR_INVALID_ARG, "codebooks must live on the same GPU device");
@@ -401,7 +408,7 @@ tq_status prepare_decode(const tq_codebook *kcb, const tq_codebook *vcb, const v
   if (v == nullptr || out == nullptr) return fail(TQ_ERR_INVALID_ARG, "NULL argument");
   if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad out_dtype");
   tq::DecodeArgs a{};
-  const tq_status st = prepare_keys(kcb, q, q_dtype, k, seq_len, batch, n_q_heads, n_kv_heads, softmax_scale,
+  const tq_status st = prepare_keys(kcb, q, q_dtype, k, seq_len, batch, n_q_heads, n_kv_heads, n_new, softmax_scale,
                                     dbg_scores, workspace, workspace_bytes, &a);
   if (st != TQ_OK) return st;
   if (v->t_cap != k->t_cap) return fail(TQ_ERR_INVALID_ARG, "key/value t_cap must match");
@@ -437,8 +444,19 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
                               tq_dtype out_dtype, float *dbg_scores, void *workspace, size_t workspace_bytes,
                               void *stream) {
   tq::DecodeArgs a{};
-  const tq_status st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, softmax_scale,
-                                      out, out_dtype, dbg_scores, workspace, workspace_bytes, &a);
+  const tq_status st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, 1,
+                                      softmax_scale, out, out_dtype, dbg_scores, workspace, workspace_bytes, &a);
+  if (st != TQ_OK) return st;
+  return run_decode(kcb, a, stream);
+}
+
+tq_status tq_chunk_attention(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
+                             const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, int32_t n_new, float softmax_scale, void *out,
+                             tq_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  tq::DecodeArgs a{};
+  const tq_status st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, n_new,
+                                      softmax_scale, out, out_dtype, nullptr, workspace, workspace_bytes, &a);
   if (st != TQ_OK) return st;
   return run_decode(kcb, a, stream);
 }
@@ -449,8 +467,8 @@ tq_status tq_append_decode(const tq_codebook *kcb, const tq_codebook *vcb, const
                            float softmax_scale, void *out, tq_dtype out_dtype, void *workspace,
                            size_t workspace_bytes, void *stream) {
   tq::DecodeArgs da{};
-  tq_status st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, softmax_scale, out,
-                                out_dtype, nullptr, workspace, workspace_bytes, &da);
+  tq_status st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, 1, softmax_scale,
+                                out, out_dtype, nullptr, workspace, workspace_bytes, &da);
   if (st != TQ_OK) return st;
   if (k_new == nullptr || v_new == nullptr) return fail(TQ_ERR_INVALID_ARG, "k_new and v_new are required");
   const int64_t n = static_cast<int64_t>(batch) * n_kv_heads;
@@ -482,8 +500,8 @@ tq_status tq_attention_logits(const tq_codebook *kcb, const void *q, tq_dtype q_
                               void *stream) {
   if (logits == nullptr) return fail(TQ_ERR_INVALID_ARG, "logits is NULL");
   tq::DecodeArgs a{};
-  const tq_status st = prepare_keys(kcb, q, q_dtype, k, seq_len, batch, n_q_heads, n_kv_heads, softmax_scale, logits,
-                                    workspace, workspace_bytes, &a);
+  const tq_status st = prepare_keys(kcb, q, q_dtype, k, seq_len, batch, n_q_heads, n_kv_heads, 1, softmax_scale,
+                                    logits, workspace, workspace_bytes, &a);
   if (st != TQ_OK) return st;
   DeviceGuard guard(kcb->device);
   if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));

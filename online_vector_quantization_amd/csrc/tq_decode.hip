@@ -282,7 +282,8 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   __shared__ float s_ml[kWaves][G][2];
 
   const int chunk_id = blockIdx.x;
-  const int hk = blockIdx.y;
+  const int hk = blockIdx.y / a.n_new;        // kv head
+  const int jq = blockIdx.y - hk * a.n_new;   // query of the chunk: position seq_len - n_new + jq
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -290,10 +291,12 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   const int hq0 = hk * G;
   const int VB = a.v_bits;
   const int VW = 4 * VB;
-  const int row_id = b * a.n_kv_heads + hk;             // (b, kv head)
-  const int group_id = row_id * a.n_chunks + chunk_id;  // this work-group
+  const int row_id = b * a.n_kv_heads + hk;             // (b, kv head): the cache row
+  const int qrow = row_id * a.n_new + jq;               // (b, kv head, query)
+  const int group_id = qrow * a.n_chunks + chunk_id;    // this work-group
 
-  int T = a.seq_len[b] + a.seq_add;
+  // causal window: the query at position p sees cached tokens 0 .. p
+  int T = a.seq_len[b] + a.seq_add - (a.n_new - 1 - jq);
   T = T < 0 ? 0 : (T > a.t_cap ? static_cast<int>(a.t_cap) : T);
   const int t_begin = chunk_id * a.chunk;
   const int t_end = min(T, t_begin + a.chunk);
@@ -315,7 +318,8 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
     for (int jj = 0; jj < kJ; ++jj) sv[jj] = a.qjl_rot_t[(kJ * part + jj) * kQjlDim + pi_];
   }
   for (int e = tid; e < G * D; e += kThreads)
-    sh.pro.q[e / D][e % D] = load_q(a.q, a.q_bf16, static_cast<int64_t>(b * a.n_q_heads + hq0) * D + e);
+    sh.pro.q[e / D][e % D] =
+        load_q(a.q, a.q_bf16, (static_cast<int64_t>(b * a.n_q_heads + hq0 + e / D) * a.n_new + jq) * D + e % D);
   {
     // dequantization tables, precomputed per codebook
     const uint4 *kl = reinterpret_cast<const uint4 *>(a.k_lut);
@@ -533,7 +537,7 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
       for (int h = 0; h < G; ++h) {
         l[h] = valid ? a.scale * nu * dot[h] : -INFINITY;
         if ((SC || a.scores != nullptr) && valid)
-          a.scores[(static_cast<int64_t>(b) * a.n_q_heads + hq0 + h) * a.t_cap + t] = l[h];
+          a.scores[((static_cast<int64_t>(b) * a.n_q_heads + hq0 + h) * a.n_new + jq) * a.t_cap + t] = l[h];
       }
     }
     if constexpr (SC) {
@@ -670,15 +674,16 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
   __shared__ float s_o[4][D];
   __shared__ float s_r[4][D];
   __shared__ float s_scal[2];
-  const int bhq = blockIdx.x;                  // b * Hq + q head
-  const int b = bhq / a.n_q_heads;
-  const int hq = bhq % a.n_q_heads;
+  const int bhq = blockIdx.x;                  // (b * Hq + q head) * n_new + query
+  const int jq = bhq % a.n_new;
+  const int b = bhq / a.n_new / a.n_q_heads;
+  const int hq = bhq / a.n_new % a.n_q_heads;
   const int g = a.n_q_heads / a.n_kv_heads;
   const int hk = hq / g, h = hq % g;
-  const int row_id = b * a.n_kv_heads + hk;
+  const int qrow = (b * a.n_kv_heads + hk) * a.n_new + jq;
   const int tid = threadIdx.x;
   const int nc = a.n_chunks;
-  const int64_t grp0 = static_cast<int64_t>(row_id) * nc;
+  const int64_t grp0 = static_cast<int64_t>(qrow) * nc;
   // thread (i, quarter): output coordinate i; chunks quarter, quarter + 4, ...;
   // Pi_v rows 32 quarter .. 32 quarter + 31 of column i
   const int i = tid & (D - 1), quarter = tid >> 7;
@@ -744,7 +749,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
   }
   // Append steps: the sequence has one more cached token (the main kernel,
   // the only reader of seq_len, has completed).
-  if (a.seq_inc != nullptr && hq == 0 && tid == 0) {
+  if (a.seq_inc != nullptr && hq == 0 && jq == 0 && tid == 0) {
     const int32_t s = a.seq_inc[b];
     if (s >= 0 && s < a.t_cap) a.seq_inc[b] = s + 1;
   }
@@ -770,8 +775,8 @@ hipError_t launch_q(const DecodeArgs &a, int g, dim3 grid, hipStream_t stream) {
 template <bool SC>
 hipError_t launch_main(const DecodeArgs &a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
-  if (a.n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
-  const dim3 grid(a.n_chunks, a.n_kv_heads, a.batch);
+  if (a.n_chunks > kMaxDecodeChunks || a.n_new < 1 || a.n_kv_heads * a.n_new > 65535) return hipErrorInvalidValue;
+  const dim3 grid(a.n_chunks, a.n_kv_heads * a.n_new, a.batch);
   switch (a.k_bits) {
     case 1: return launch_q<1, SC>(a, g, grid, stream);
     case 2: return launch_q<2, SC>(a, g, grid, stream);
@@ -810,7 +815,7 @@ DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int64_t t_cap) 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const hipError_t e = launch_main<false>(a, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads), dim3(kCombThreads), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads * a.n_new), dim3(kCombThreads), 0, stream, a);
   return hipGetLastError();
 }
 

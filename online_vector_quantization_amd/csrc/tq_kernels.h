@@ -98,6 +98,7 @@ struct DecodeArgs {
   int seq_add;             // tokens attended: clamp(seq_len[b] + seq_add, 0, t_cap)
   int32_t *seq_inc;        // if set: seq_len[b] += 1 after the step when 0 <= seq_len[b] < t_cap
   int batch, n_q_heads, n_kv_heads;
+  int n_new;               // queries per (b, q head); query j sits at position seq_len[b] - n_new + j
   int k_bits, v_bits, qjl_m;
   float scale;
   float qjl_coef;          // sqrt(pi/2)/m

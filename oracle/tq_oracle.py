@@ -393,6 +393,28 @@ def decode_attention(q, kcache, vcache, seq_len, kbook, vbook, scale=None, retur
     return out
 
 
+def chunk_attention(q, kcache, vcache, seq_len, kbook, vbook, scale=None):
+    """Causal attention of a chunk of n_new new queries per (b, q head) over the
+    compressed cache  [memory-wall §1: each new token attends over the keys and
+    values of every token up to itself; memory-wall §2: over the compressed
+    cache].
+
+    q[B, Hq, n_new, d].  The new tokens are the last n_new cached ones: query j
+    of sequence b sits at position p = seq_len[b] - n_new + j and sees cached
+    positions 0 .. p, i.e. clamp(p + 1, 0, Tcap) tokens (none: zero output).
+    Each query is then a single-query decode over its own prefix.
+    Returns out[B, Hq, n_new, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, n_new, d = q.shape
+    Tcap = kcache["norms"].shape[2]
+    out = np.zeros((B, Hq, n_new, d))
+    for j in range(n_new):
+        seen = [min(max(int(seq_len[b]) - n_new + j + 1, 0), Tcap) for b in range(B)]
+        out[:, :, j] = decode_attention(q[:, :, j], kcache, vcache, seen, kbook, vbook, scale=scale)
+    return out
+
+
 def exact_attention(q, k, v, scale=None):
     """Textbook softmax attention of one query over uncompressed K, V (float64)."""
     q = np.asarray(q, dtype=np.float64)

@@ -1,0 +1,122 @@
+"""tq_chunk_attention: a chunk of n_new queries per (b, q head), query j at
+position seq_len - n_new + j attending causally over the compressed cache.
+
+* Oracle parity (chunk_attention) at g = 1, 4, 8, n_new = 1, 5, 16, keys with
+  and without QJL, over ragged sequences, one shorter than the chunk (its
+  first queries see nothing and give zeros).
+* Query j equals tq_decode_attention of that query alone with
+  seq_len - n_new + j + 1 tokens: bit for bit at the small sizes, where both
+  launches split the 1100-token cache into the same three 512-token chunks;
+  within 1e-5 (relative and absolute) at full size, where the chunk launch
+  has n_new times more rows and so longer chunks (the partial sums are added
+  in another order).
+* Full size: 8 queries per head over the Llama-3-8B-shaped layer (32768
+  tokens): every query against the single-query decode, two against the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle as O  # noqa: E402
+from online_vector_quantization_amd import synth  # noqa: E402
+
+import gpu_helpers as H  # noqa: E402
+import online_vector_quantization_amd as T  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; torch sees no GPU")
+    T.load_library()
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _per_query_decode(kcb, vcb, q, kc, vc, lens):
+    """Each query of the chunk through tq_decode_attention alone."""
+    B, Hq, n_new, d = q.shape
+    outs = []
+    for j in range(n_new):
+        sl = torch.tensor([ln - n_new + j + 1 for ln in lens], dtype=torch.int32, device=H.DEV)
+        outs.append(T.decode_attention(kcb, vcb, q[:, :, j].contiguous(), kc, vc, sl))
+    return torch.stack(outs, dim=2)
+
+
+@pytest.mark.parametrize("kbits,m,vbits,g,n_new", [(2, 128, 3, 4, 5), (1, 128, 2, 8, 16), (3, 128, 4, 1, 1),
+                                                   (2, 0, 2, 4, 16), (4, 0, 3, 8, 5)])
+def test_chunk_parity(kbits, m, vbits, g, n_new):
+    B, Hkv, t_cap = 3, 2, 1100
+    lens = [1100, 3, 640]
+    Hq = Hkv * g
+    rng = np.random.default_rng(1000 + 10 * kbits + g + n_new)
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap, lognormal_sigma=0.5))
+    v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap, lognormal_sigma=0.5))
+    q = H.to_device(synth.bf16_bits(rng.standard_normal((B, Hq, n_new, 128)).astype(np.float32)), "bf16")
+    kcb, vcb = H.gpu_book(kbits, m), H.gpu_book(vbits, 0)
+    kc, vc = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, t_cap, t_cap)
+    sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+    _log(f"chunk kbits={kbits} m={m} vbits={vbits} g={g} n_new={n_new} lens={lens}")
+    got = T.chunk_attention(kcb, vcb, q, kc, vc, sl)
+    per = _per_query_decode(kcb, vcb, q, kc, vc, lens)
+    torch.cuda.synchronize()
+    g_np = got.cpu().numpy()
+    np.testing.assert_array_equal(g_np.view(np.uint32), per.cpu().numpy().view(np.uint32))
+    ref = O.chunk_attention(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), H.cache_to_host(vc),
+                            lens, H.oracle_book(kbits, m), H.oracle_book(vbits, 0))
+    err = np.abs(g_np - ref).max()
+    assert err <= 2e-3, f"max-abs error {err:.3e}"
+    # the short sequence: queries 0 .. n_new - 4 see no token
+    empty = max(0, n_new - 3)
+    assert np.all(g_np[1, :, :empty] == 0.0)
+
+
+def test_chunk_bf16_output_and_determinism():
+    B, Hkv, g, n_new, t_cap = 2, 2, 4, 7, 900
+    rng = np.random.default_rng(5)
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap))
+    v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap))
+    q = H.to_device(synth.bf16_bits(rng.standard_normal((B, Hkv * g, n_new, 128)).astype(np.float32)), "bf16")
+    kcb, vcb = H.gpu_book(2, 128), H.gpu_book(3, 0)
+    kc, vc = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, t_cap, t_cap)
+    sl = torch.tensor([900, 450], dtype=torch.int32, device=H.DEV)
+    o32 = T.chunk_attention(kcb, vcb, q, kc, vc, sl)
+    o32b = T.chunk_attention(kcb, vcb, q, kc, vc, sl)
+    o16 = T.chunk_attention(kcb, vcb, q, kc, vc, sl, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    a = o32.cpu().numpy()
+    np.testing.assert_array_equal(a.view(np.uint32), o32b.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(o16.float().cpu().numpy(), H.rne_bf16(a))
+
+
+def test_chunk_llama8b_full():
+    wl = synth.llama8b()
+    S, n_new = wl.seq_len, 8
+    _log(f"{wl.name}: {n_new} causal queries per head over {S} tokens")
+    kcb, vcb = H.gpu_book(2, 128), H.gpu_book(3, 0)
+    kc = T.CompressedCache.allocate(kcb, 1, 8, S)
+    vc = T.CompressedCache.allocate(vcb, 1, 8, S)
+    T.encode_into_cache(kcb, H.to_device(wl.k.reshape(-1, 128), "bf16"), kc)
+    T.encode_into_cache(vcb, H.to_device(wl.v.reshape(-1, 128), "bf16"), vc)
+    rng = np.random.default_rng(8)
+    q = H.to_device(synth.bf16_bits(rng.standard_normal((1, 32, n_new, 128)).astype(np.float32)), "bf16")
+    sl = torch.tensor([S], dtype=torch.int32, device=H.DEV)
+    got = T.chunk_attention(kcb, vcb, q, kc, vc, sl)
+    per = _per_query_decode(kcb, vcb, q, kc, vc, [S])
+    torch.cuda.synchronize()
+    g_np = got.cpu().numpy()
+    np.testing.assert_allclose(g_np, per.cpu().numpy(), rtol=1e-5, atol=1e-5)
+    q_host = q.float().cpu().numpy().astype(np.float64)
+    kh, vh = H.cache_to_host(kc), H.cache_to_host(vc)
+    for j in (0, n_new - 1):
+        ref = O.decode_attention(q_host[:, :, j], kh, vh, [S - n_new + j + 1], H.oracle_book(2, 128),
+                                 H.oracle_book(3, 0))
+        err = np.abs(g_np[:, :, j] - ref).max()
+        _log(f"  query {j}: max-abs error {err:.2e}")
+        assert err <= 2e-3

@@ -479,3 +479,36 @@ def test_decode_empty_sequence_gives_zero():
     vb = {"bits": 1, "centroids": cv, "Pi": Pi}
     out = O.decode_attention(rng.standard_normal((1, 2, d)), kc, vc, [0], kb, vb)
     assert np.all(out == 0.0)
+
+
+def test_chunk_attention_is_causal_masked_attention():
+    # Lossless codes, no QJL term: the chunk's output must equal textbook
+    # attention of the n_new queries with the standard causal mask (query j at
+    # position seq_len - n_new + j sees keys at positions <= its own), written
+    # here as one masked score matrix per (b, head), including a sequence
+    # shorter than the chunk (its first queries see nothing: zero output).
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, T, d, n_new = 3, 4, 2, 23, 16, 5
+    Pi = O.haar_rotation(d, 4)
+    K, V, kc, vc, ck, cv = _lossless_cache(rng, B, Hkv, T, d, 2, 2, Pi)
+    q = rng.standard_normal((B, Hq, n_new, d))
+    seq_len = [T, 12, 3]
+    kb = {"bits": 2, "centroids": ck, "Pi": Pi, "S": None}
+    vb = {"bits": 2, "centroids": cv, "Pi": Pi}
+    out = O.chunk_attention(q, kc, vc, seq_len, kb, vb)
+    g = Hq // Hkv
+    for b in range(B):
+        pos = seq_len[b] - n_new + np.arange(n_new)           # query positions
+        for h in range(Hq):
+            s = q[b, h] @ K[b, h // g].T / math.sqrt(d)       # [n_new, T]
+            mask = np.arange(T)[None, :] <= pos[:, None]
+            s = np.where(mask, s, -np.inf)
+            for j in range(n_new):
+                if not mask[j].any():
+                    assert np.all(out[b, h, j] == 0.0)
+                    continue
+                w = np.exp(s[j] - s[j].max())
+                np.testing.assert_allclose(out[b, h, j], (w / w.sum()) @ V[b, h // g], rtol=1e-11, atol=1e-12)
+    # the last query of the chunk is the single-query decode over seq_len
+    dec = O.decode_attention(q[:, :, -1], kc, vc, seq_len, kb, vb)
+    np.testing.assert_allclose(out[:, :, -1], dec, rtol=0, atol=0)
