@@ -5,11 +5,10 @@ position seq_len - n_new + j attending causally over the compressed cache.
   and without QJL, over ragged sequences, one shorter than the chunk (its
   first queries see nothing and give zeros).
 * Query j equals tq_decode_attention of that query alone with
-  seq_len - n_new + j + 1 tokens: bit for bit at the small sizes, where both
-  launches split the 1100-token cache into the same three 512-token chunks;
-  within 1e-5 (relative and absolute) at full size, where the chunk launch
-  has n_new times more rows and so longer chunks (the partial sums are added
-  in another order).
+  seq_len - n_new + j + 1 tokens: bit for bit for n_new = 1 (same launch
+  plan), else within 1e-5 relative and absolute (the chunk launch has n_new
+  times more rows, so its token chunks may be longer and the partial sums
+  are then added in another order).
 * Full size: 8 queries per head over the Llama-3-8B-shaped layer (32768
   tokens): every query against the single-query decode, two against the oracle.
 """
@@ -67,7 +66,10 @@ def test_chunk_parity(kbits, m, vbits, g, n_new):
     per = _per_query_decode(kcb, vcb, q, kc, vc, lens)
     torch.cuda.synchronize()
     g_np = got.cpu().numpy()
-    np.testing.assert_array_equal(g_np.view(np.uint32), per.cpu().numpy().view(np.uint32))
+    if n_new == 1:
+        np.testing.assert_array_equal(g_np.view(np.uint32), per.cpu().numpy().view(np.uint32))
+    else:
+        np.testing.assert_allclose(g_np, per.cpu().numpy(), rtol=1e-5, atol=1e-5)
     ref = O.chunk_attention(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), H.cache_to_host(vc),
                             lens, H.oracle_book(kbits, m), H.oracle_book(vbits, 0))
     err = np.abs(g_np - ref).max()
