@@ -282,7 +282,7 @@ def chunk_only(T, kcb, vcb, caches, S, Hq, args, dev):
     q = torch.randn(B, Hq, n_new, 128, generator=g, device=dev).to(torch.bfloat16)
     seq = torch.full((B,), S, dtype=torch.int32, device=dev)
     out = torch.empty(B, Hq, n_new, 128, dtype=torch.bfloat16, device=dev)
-    ws = T.alloc_workspace(B * n_new, Hq, kc0.codes.shape[1], kc0.t_cap, dev)
+    ws = T.alloc_chunk_workspace(B, Hq, kc0.codes.shape[1], n_new, kc0.t_cap, dev)
     run = lambda s: T.chunk_attention(kcb, vcb, q, caches[s % len(caches)][0], caches[s % len(caches)][1], seq,
                                       out=out, workspace=ws, stream=stream)
     for s in range(args.warmup):

@@ -186,19 +186,25 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
  *   n_new         >= 1, with n_new * n_kv_heads <= 65535, batch <= 65535 and
  *                 batch * n_q_heads * n_new <= 2^24 (else TQ_ERR_INVALID_ARG).
  *   out           device [batch][n_q_heads][n_new][d] of out_dtype.
- *   workspace     at least tq_decode_workspace_bytes(batch * n_new, n_q_heads,
- *                 n_kv_heads, t_cap) bytes, 256-byte aligned; calls that share
- *                 it must not overlap in time.
- * Other arguments as in tq_decode_attention.  With n_new = 1 the result equals
- * tq_decode_attention bit for bit.  Query j's result equals tq_decode_attention
- * of that query alone with seq_len[b] - n_new + j + 1 tokens up to the order of
- * the split sums: the token chunks are sized for the whole launch, so they
- * match (and the results are bitwise equal) only when both launches pick the
- * same chunk length. */
+ *   workspace     at least tq_chunk_workspace_bytes bytes for the same sizes,
+ *                 256-byte aligned; calls that share it must not overlap in time.
+ * Other arguments as in tq_decode_attention.
+ * With n_new * (n_q_heads / n_kv_heads) < 16 the queries run through the
+ * decode kernel: n_new = 1 equals tq_decode_attention bit for bit, and query
+ * j equals tq_decode_attention of that query alone with seq_len[b] - n_new +
+ * j + 1 tokens up to the order of the split sums (bitwise when both launches
+ * pick the same token-chunk length).  From 16 query rows per kv head on, the
+ * matrix cores compute the scores and the value sum with bf16 hi/lo operand
+ * splits (three products per fp32 product, about 2^-16 relative error per
+ * product); the result agrees with the single-query path to about 1e-5. */
 tq_status tq_chunk_attention(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
                              const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
                              int32_t n_q_heads, int32_t n_kv_heads, int32_t n_new, float softmax_scale, void *out,
                              tq_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace tq_chunk_attention needs for these sizes. */
+tq_status tq_chunk_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t n_new,
+                                   int64_t t_cap, size_t *bytes);
 
 /* One step of a decode loop, enqueued on `stream` with no host synchronization
  * (so a caller can capture it in a graph and replay it): the new key and value

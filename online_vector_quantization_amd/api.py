@@ -24,7 +24,8 @@ TQ_F32, TQ_BF16 = 0, 1
 EXPORTED = (
     "tq_codebook_build", "tq_codebook_free", "tq_codebook_info", "tq_codebook_export",
     "tq_codebook_export_f64", "tq_record_words", "tq_encode_kv", "tq_decode_workspace_bytes",
-    "tq_decode_attention", "tq_append_decode", "tq_attention_logits", "tq_chunk_attention", "tq_status_string", "tq_last_error",
+    "tq_decode_attention", "tq_append_decode", "tq_attention_logits", "tq_chunk_attention",
+    "tq_chunk_workspace_bytes", "tq_status_string", "tq_last_error",
 )
 
 
@@ -64,6 +65,7 @@ def load_library() -> ctypes.CDLL:
                                         i32, i32, i32, f32, vp, i32, vp, vp, ctypes.c_size_t, vp]
     lib.tq_append_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache),
                                      vp, i32, i32, i32, f32, vp, i32, vp, ctypes.c_size_t, vp]
+    lib.tq_chunk_workspace_bytes.argtypes = [i32, i32, i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_chunk_attention.argtypes = [vp, vp, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache), vp,
                                        i32, i32, i32, i32, f32, vp, i32, vp, ctypes.c_size_t, vp]
     lib.tq_attention_logits.argtypes = [vp, vp, i32, ctypes.POINTER(TqCache), vp, i32, i32, i32, f32, vp, vp,
@@ -238,6 +240,19 @@ def alloc_workspace(batch: int, n_q_heads: int, n_kv_heads: int, t_cap: int, dev
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def chunk_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, n_new: int, t_cap: int) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().tq_chunk_workspace_bytes(batch, n_q_heads, n_kv_heads, n_new, t_cap, ctypes.byref(out)),
+           "tq_chunk_workspace_bytes")
+    return out.value
+
+
+def alloc_chunk_workspace(batch: int, n_q_heads: int, n_kv_heads: int, n_new: int, t_cap: int, device):
+    """Device scratch for tq_chunk_attention."""
+    return torch.empty(chunk_workspace_bytes(batch, n_q_heads, n_kv_heads, n_new, t_cap), dtype=torch.uint8,
+                       device=device)
+
+
 def decode_attention(kcb: Codebook, vcb: Codebook, q: torch.Tensor, kcache: CompressedCache,
                      vcache: CompressedCache, seq_len: torch.Tensor, out: Optional[torch.Tensor] = None,
                      softmax_scale: float = 0.0, out_dtype=torch.float32,
@@ -278,7 +293,7 @@ def chunk_attention(kcb: Codebook, vcb: Codebook, q: torch.Tensor, kcache: Compr
     if out is None:
         out = torch.empty(B, Hq, n_new, d, dtype=out_dtype, device=q.device)
     if workspace is None:
-        workspace = alloc_workspace(B * n_new, Hq, Hkv, kcache.t_cap, q.device)
+        workspace = alloc_chunk_workspace(B, Hq, Hkv, n_new, kcache.t_cap, q.device)
     _require_cuda(q, seq_len, out, workspace, kcache.codes, vcache.codes)
     ks, vs = kcache.as_struct(), vcache.as_struct()
     _check(load_library().tq_chunk_attention(
@@ -349,6 +364,11 @@ def compressed_bytes_per_token(kcb: Codebook, vcb: Codebook) -> int:
     k = 4 * kcb.code_words + 4 * kcb.sign_words + 4 + (4 if kcb.qjl_dim else 0)
     v = 4 * vcb.code_words + 4
     return k + v
+
+
+def chunk_uses_mfma(g: int, n_new: int) -> bool:
+    """Whether tq_chunk_attention takes its matrix-core kernel (16 or more query rows per kv head)."""
+    return g * n_new >= 16
 
 
 def qjl_coefficient(m: int) -> float:

@@ -359,7 +359,7 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
       (k->res_norms && !aligned(k->res_norms, 4)) || !aligned(q, 4) || !aligned(workspace, 256) ||
       !aligned(seq_len, 4) || (scores && !aligned(scores, 4)))
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer");
-  const tq::DecodePlan plan = tq::plan_decode(batch * n_new, n_q_heads, n_kv_heads, k->t_cap);
+  const tq::DecodePlan plan = tq::plan_chunk(batch, n_q_heads, n_kv_heads, n_new, k->t_cap);
   if (workspace_bytes < plan.total_bytes)
     return fail(TQ_ERR_INVALID_ARG, "workspace too small (%zu < %zu)", workspace_bytes, plan.total_bytes);
   tq::DecodeArgs a{};
@@ -383,10 +383,12 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
   a.rot_k_t = dev_ptr<float>(kcb, kcb->off_rot_t_f32);
   a.qjl_rot_t = m > 0 ? dev_ptr<float>(kcb, kcb->off_qjl_rot_t_f32) : nullptr;
   a.k_lut = dev_ptr<float>(kcb, kcb->off_key_lut);
+  a.k_pair = dev_ptr<float>(kcb, kcb->off_pair_lut);
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   a.ws_qslot = reinterpret_cast<float *>(ws + plan.off_qslot);
   a.ws_part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
   a.ws_part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
+  a.ws_qprep = tq::chunk_uses_mfma(g, n_new) ? reinterpret_cast<float *>(ws + plan.off_qprep) : nullptr;
   a.chunk = plan.chunk;
   a.n_chunks = plan.n_chunks;
   *out_args = a;
@@ -458,7 +460,22 @@ tq_status tq_chunk_attention(const tq_codebook *kcb, const tq_codebook *vcb, con
   const tq_status st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, n_new,
                                       softmax_scale, out, out_dtype, nullptr, workspace, workspace_bytes, &a);
   if (st != TQ_OK) return st;
-  return run_decode(kcb, a, stream);
+  if (!tq::chunk_uses_mfma(n_q_heads / n_kv_heads, n_new)) return run_decode(kcb, a, stream);
+  DeviceGuard guard(kcb->device);
+  if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
+  const hipError_t e = tq::launch_chunk_mfma(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "chunk attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+tq_status tq_chunk_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t n_new, int64_t t_cap,
+                                   size_t *bytes) {
+  if (bytes == nullptr) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || t_cap < 1 || n_new < 1 || n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d/%d, n_new %d, t_cap %lld)", batch, n_q_heads,
+                n_kv_heads, n_new, static_cast<long long>(t_cap));
+  *bytes = tq::plan_chunk(batch, n_q_heads, n_kv_heads, n_new, t_cap).total_bytes;
+  return ok();
 }
 
 tq_status tq_append_decode(const tq_codebook *kcb, const tq_codebook *vcb, const void *k_new, const void *v_new,

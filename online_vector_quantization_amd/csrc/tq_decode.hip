@@ -45,8 +45,6 @@ namespace tq {
 namespace {
 
 constexpr int D = kHeadDim;
-// Waves per work-group (8: each wave usually gets several 64-token tiles,
-// which amortizes the per-wave prologue and merge).
 // Waves per work-group.  8 for every g: 12 (g = 2, 4) and 16 (g = 1) fit the
 // registers too, but measured no faster (the 8B-layer decode took 7% longer).
 constexpr int decode_waves(int) { return 8; }
@@ -817,15 +815,27 @@ DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int64_t t_cap) 
   p.off_qslot = 0;
   p.off_part_o = align(p.off_qslot + static_cast<size_t>(groups) * g * D * sizeof(float));
   p.off_part_ml = align(p.off_part_o + static_cast<size_t>(groups) * g * D * sizeof(float));
+  p.off_qprep = 0;
   p.total_bytes = align(p.off_part_ml + static_cast<size_t>(groups) * g * 2 * sizeof(float));
   return p;
+}
+
+DecodePlan plan_chunk(int batch, int n_q_heads, int n_kv_heads, int n_new, int64_t t_cap) {
+  const int g = n_q_heads / std::max(1, n_kv_heads);
+  return chunk_uses_mfma(g, n_new) ? plan_chunk_mfma(batch, n_q_heads, n_kv_heads, n_new, t_cap)
+                                   : plan_decode(batch * n_new, n_q_heads, n_kv_heads, t_cap);
+}
+
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
+  if (a.n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads * a.n_new), dim3(kCombThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const hipError_t e = launch_main<false>(a, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads * a.n_new), dim3(kCombThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_combine(a, stream);
 }
 
 hipError_t launch_logits(const DecodeArgs &a, hipStream_t stream) {

@@ -79,10 +79,20 @@ struct DecodePlan {
   size_t off_qslot;        // bytes into the workspace: float[groups][d][g], q~ per work-group (coordinate-major)
   size_t off_part_o;       // float[groups][g][d]: rotated partial outputs
   size_t off_part_ml;      // float[groups][g][2]: running max and sum
+  size_t off_qprep;        // chunk attention on the matrix cores: float[B*Hq*n_new][2d], (q~, s) per query
   size_t total_bytes;
 };
 
 DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int64_t t_cap);
+
+// Chunk attention: the matrix-core kernel serves n_new * g >= kChunkMfmaRows
+// query rows per kv head; fewer go through the decode kernel (one work-group
+// per (kv head, query)).
+constexpr int kChunkMfmaRows = 16;
+inline bool chunk_uses_mfma(int g, int n_new) { return g * n_new >= kChunkMfmaRows; }
+DecodePlan plan_chunk_mfma(int batch, int n_q_heads, int n_kv_heads, int n_new, int64_t t_cap);
+// The plan tq_chunk_attention runs with (either kind).
+DecodePlan plan_chunk(int batch, int n_q_heads, int n_kv_heads, int n_new, int64_t t_cap);
 
 struct DecodeArgs {
   const void *q;
@@ -110,9 +120,11 @@ struct DecodeArgs {
   const float *rot_v;      // Pi_v row-major (d x d)
   const float *k_lut;      // key dequantization table (kKeyLutBytes)
   const float *v_lut;      // value pair table (kPairLutBytes)
+  const float *k_pair;     // key pair table (kPairLutBytes layout, key codebook)
   float *ws_qslot;
   float *ws_part_o;        // [B*Hkv][n_chunks][g][d]
   float *ws_part_ml;       // [B*Hkv][n_chunks][g][2]
+  float *ws_qprep;         // chunk attention on the matrix cores: (q~, s) per query row
   int chunk, n_chunks;
 };
 
@@ -120,5 +132,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // Scores only: the decode's key phase, writing every l_t to a.scores (no value
 // phase, no combine; the value fields are not read).
 hipError_t launch_logits(const DecodeArgs &a, hipStream_t stream);
+// The merge of the chunk partials (log-sum-exp, Pi_v^T, output; seq_inc).
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
+// Chunk attention on the matrix cores: query prep, the tiles, the merge.
+hipError_t launch_chunk_mfma(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace tq

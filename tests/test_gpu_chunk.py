@@ -6,11 +6,14 @@ position seq_len - n_new + j attending causally over the compressed cache.
   first queries see nothing and give zeros).
 * Query j equals tq_decode_attention of that query alone with
   seq_len - n_new + j + 1 tokens: bit for bit for n_new = 1 (same launch
-  plan), else within 1e-5 relative and absolute (the chunk launch has n_new
-  times more rows, so its token chunks may be longer and the partial sums
-  are then added in another order).
-* Full size: 8 queries per head over the Llama-3-8B-shaped layer (32768
-  tokens): every query against the single-query decode, two against the oracle.
+  plan); within 1e-5 relative and absolute while fewer than 16 query rows per
+  kv head run through the decode kernel (longer token chunks add the partial
+  sums in another order); within the 2e-3 output bar on the matrix-core path,
+  whose bf16 hi/lo products carry about 1e-5 relative error into the logits
+  (5e-4 at the full 8B layer, whose outlier channels make large logits).
+* Full size: 8 queries per head (32 rows per kv head: the matrix-core path)
+  over the Llama-3-8B-shaped layer (32768 tokens): every query against the
+  single-query decode, two against the oracle.
 """
 import sys
 
@@ -66,13 +69,18 @@ def test_chunk_parity(kbits, m, vbits, g, n_new):
     per = _per_query_decode(kcb, vcb, q, kc, vc, lens)
     torch.cuda.synchronize()
     g_np = got.cpu().numpy()
+    p_np = per.cpu().numpy()
+    _log(f"  vs single-query decode: max-abs {np.abs(g_np - p_np).max():.2e} (max |o| {np.abs(p_np).max():.2e})")
     if n_new == 1:
-        np.testing.assert_array_equal(g_np.view(np.uint32), per.cpu().numpy().view(np.uint32))
-    else:
-        np.testing.assert_allclose(g_np, per.cpu().numpy(), rtol=1e-5, atol=1e-5)
+        np.testing.assert_array_equal(g_np.view(np.uint32), p_np.view(np.uint32))
+    elif not T.api.chunk_uses_mfma(g, n_new):
+        np.testing.assert_allclose(g_np, p_np, rtol=1e-5, atol=1e-5)
+    else:   # both sides within the 2e-3 output bar of the oracle; observed 3e-5 .. 6e-5 here
+        np.testing.assert_allclose(g_np, p_np, rtol=0, atol=2e-3)
     ref = O.chunk_attention(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), H.cache_to_host(vc),
                             lens, H.oracle_book(kbits, m), H.oracle_book(vbits, 0))
     err = np.abs(g_np - ref).max()
+    _log(f"  vs oracle: max-abs {err:.2e}")
     assert err <= 2e-3, f"max-abs error {err:.3e}"
     # the short sequence: queries 0 .. n_new - 4 see no token
     empty = max(0, n_new - 3)
@@ -113,7 +121,8 @@ def test_chunk_llama8b_full():
     per = _per_query_decode(kcb, vcb, q, kc, vc, [S])
     torch.cuda.synchronize()
     g_np = got.cpu().numpy()
-    np.testing.assert_allclose(g_np, per.cpu().numpy(), rtol=1e-5, atol=1e-5)
+    _log(f"  vs single-query decode: max-abs {np.abs(g_np - per.cpu().numpy()).max():.2e}")
+    np.testing.assert_allclose(g_np, per.cpu().numpy(), rtol=0, atol=2e-3)
     q_host = q.float().cpu().numpy().astype(np.float64)
     kh, vh = H.cache_to_host(kc), H.cache_to_host(vc)
     for j in (0, n_new - 1):
