@@ -21,19 +21,20 @@
 // token chunks, Pi_v^T, output).
 //
 // Tile kernel: work-group = (64 query rows of one kv head, chunk of tokens),
-// 4 waves.  Row m of kv head hk is query j = m / g of q head hk g + m % g, at
-// position seq_len - n_new + j; it sees tokens below
-// clamp(seq_len - n_new + j + 1, 0, t_cap).  Per 64-token tile:
-//   1. the tile's key and value records are staged in LDS;
+// 8 waves (two per SIMD).  Row m of kv head hk is query j = m / g of q head
+// hk g + m % g, at position seq_len - n_new + j; it sees tokens below
+// clamp(seq_len - n_new + j + 1, 0, t_cap).  Per 128-token tile:
+//   1. the tile's key and value records are staged in LDS (and the next
+//      tile's are requested);
 //   2. the values are dequantized into a transposed (coordinate x token)
 //      bf16 hi/lo tile;
-//   3. wave (row half, token half) computes its 32 x 32 score block from
+//   3. wave (row half, token quarter) computes its 32 x 32 score block from
 //      key codes dequantized straight into MFMA operands, scales and masks
 //      it, and stores it in LDS;
-//   4. four threads per row run the online softmax over the 64 tokens and
+//   4. eight threads per row run the online softmax over the 128 tokens and
 //      store P = p nu^v as bf16 hi/lo;
-//   5. wave (row half, coordinate half) rescales and accumulates its two
-//      32 x 32 output blocks: P x V.
+//   5. wave (row half, coordinate quarter) rescales (when a running max
+//      moved) and accumulates its 32 x 32 output block: P x V.
 // The chunk's (max, sum, rotated output) per row go to the workspace in the
 // decode's partial layout.
 #include <hip/hip_runtime.h>
@@ -48,12 +49,14 @@ namespace {
 
 constexpr int D = kHeadDim;
 constexpr int kRows = 64;               // query rows per work-group
-constexpr int kTile = 64;               // tokens per tile
-constexpr int kThreads = 256;           // 4 waves
+constexpr int kTile = 128;              // tokens per tile
+constexpr int kThreads = 512;           // 8 waves
+constexpr int kSmT = kThreads / kRows;  // softmax threads per row (16 tokens each)
 constexpr int kVtStride = kTile + 8;    // bf16 per coordinate row of the value tile (16 B pad)
 constexpr int kPStride = kTile + 8;     // bf16 per row of P
 constexpr int kScStride = kTile + 4;    // floats per row of the score tile
 constexpr int kQpStride = 2 * D;        // floats per query row in the prep buffer: q~ then s
+constexpr int kSStride = D + 8;         // bf16 per row of the LDS copy of s (16 B pad)
 // A row's running max is raised only when a score exceeds it by more than
 // this (weights stay <= e^8), so most tiles rescale nothing.
 constexpr float kLazy = 8.f;
@@ -143,6 +146,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
   uint16_t *const s_ph = s_tile.p.h;
   uint16_t *const s_pl = s_tile.p.l;
   __shared__ float s_alpha[kRows];
+  // the QJL query operand s as bf16 hi/lo, [row][coordinate]: read per k-step
+  // (in registers it would not fit beside q~ at two waves per SIMD)
+  __shared__ __align__(16) uint16_t s_sh[QJL ? kRows * kSStride : 8];
+  __shared__ __align__(16) uint16_t s_sl[QJL ? kRows * kSStride : 8];
   __shared__ int s_rescale;   // some row of the tile raised its running max
 
   const int g = a.n_q_heads / a.n_kv_heads;
@@ -155,8 +162,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int mblk = wave & 1;             // row half (scores and P x V)
-  const int nb = wave >> 1;              // token half (scores)
-  const int cb0 = 2 * (wave >> 1);       // first of two 32-coordinate blocks (P x V)
+  const int nb = wave >> 1;              // token quarter (scores)
+  const int cb = wave >> 1;              // 32-coordinate block (P x V)
   const int VB = a.v_bits, VW = 4 * VB;
   const int row_id = b * a.n_kv_heads + hk;
   const int64_t row0 = static_cast<int64_t>(row_id) * a.t_cap;
@@ -186,7 +193,26 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
   }
   // A operands of the scores: row 32 mblk + l32 of the block, coordinates
   // 16 ks + 8 hi .. + 7 of q~ (and of s)
-  bf16x8 qa_h[8], qa_l[8], sa_h[QJL ? 8 : 1], sa_l[QJL ? 8 : 1];
+  bf16x8 qa_h[8], qa_l[8];
+  if constexpr (QJL) {
+    // thread: row tid / 8, coordinates 16 (tid % 8) .. + 15 of s
+    const int r = tid >> 3, c0 = 16 * (tid & 7);
+    const bool live = m0 + r < rows_total;
+    const float *sp = a.ws_qprep + (static_cast<int64_t>(row_id) * rows_total + (live ? m0 + r : 0)) * kQpStride + D + c0;
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float4 v = live ? reinterpret_cast<const float4 *>(sp)[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      split_pair(v.x, v.y, h[2 * k4], l[2 * k4]);
+      split_pair(v.z, v.w, h[2 * k4 + 1], l[2 * k4 + 1]);
+    }
+    uint4 *dh = reinterpret_cast<uint4 *>(&s_sh[r * kSStride + c0]);
+    uint4 *dl = reinterpret_cast<uint4 *>(&s_sl[r * kSStride + c0]);
+    dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
+    dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
+    dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
+    dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+  }
   {
     const int mq = m0 + 32 * mblk + l32;
     const bool live = mq < rows_total;
@@ -205,33 +231,18 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
       split_pair(x1.z, x1.w, h[3], l[3]);
       qa_h[ks] = as_bf16x8(h[0], h[1], h[2], h[3]);
       qa_l[ks] = as_bf16x8(l[0], l[1], l[2], l[3]);
-      if constexpr (QJL) {
-        float4 y0 = make_float4(0.f, 0.f, 0.f, 0.f), y1 = y0;
-        if (live) {
-          y0 = *reinterpret_cast<const float4 *>(qp + D + 16 * ks + 8 * hi);
-          y1 = *reinterpret_cast<const float4 *>(qp + D + 16 * ks + 8 * hi + 4);
-        }
-        split_pair(y0.x, y0.y, h[0], l[0]);
-        split_pair(y0.z, y0.w, h[1], l[1]);
-        split_pair(y1.x, y1.y, h[2], l[2]);
-        split_pair(y1.z, y1.w, h[3], l[3]);
-        sa_h[ks] = as_bf16x8(h[0], h[1], h[2], h[3]);
-        sa_l[ks] = as_bf16x8(l[0], l[1], l[2], l[3]);
-      }
     }
   }
   // softmax role: row sm of the block, tokens 16 sq .. 16 sq + 15 of a tile
-  const int sm = tid >> 2, sq = tid & 3;
+  const int sm = tid / kSmT, sq = tid % kSmT;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x16 o[2];
+  f32x16 o;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[c][r] = 0.f;
+  for (int r = 0; r < 16; ++r) o[r] = 0.f;
 
   // A tile's records, one thread's share (tokens past the tile's end read as
   // zero codes): at most one uint4 of key codes and one of value codes (a
-  // tile holds 16 KW and 16 VW of them), and for threads < 64 the token's
+  // tile holds 32 KW and 32 VW of them), and for threads < 128 the token's
   // sign words and norms.  Loaded one tile ahead.
   struct Rec {
     uint4 kc, vc, sg;
@@ -279,10 +290,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
 
     // ---- 2. values -> transposed bf16 hi/lo tile [coordinate][token]
     {
-      const int tok = tid & 63;
+      const int tok = tid & (kTile - 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int grp = (tid >> 6) + 4 * i;   // coordinates 8 grp .. 8 grp + 7
+        const int grp = tid / kTile + 4 * i;   // coordinates 8 grp .. 8 grp + 7
         const int bit = 8 * grp * VB;
         const int w = bit >> 5, sh = bit & 31;
         const uint32_t w0 = s_vc[tok * VW + w];
@@ -338,8 +349,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
           for (int p = 0; p < 4; ++p)
             z[p] = 0xBF80BF80u ^ (((b8 >> (2 * p)) & 1u) << 15) ^ (((b8 >> (2 * p + 1)) & 1u) << 31);
           const bf16x8 zb = as_bf16x8(z[0], z[1], z[2], z[3]);
-          tacc = mfma(sa_h[ks], zb, tacc);
-          tacc = mfma(sa_l[ks], zb, tacc);
+          const int srow = (32 * mblk + l32) * kSStride + 16 * ks + 8 * hi;
+          tacc = mfma(*reinterpret_cast<const bf16x8 *>(&s_sh[srow]), zb, tacc);
+          tacc = mfma(*reinterpret_cast<const bf16x8 *>(&s_sl[srow]), zb, tacc);
         }
       }
       const float nu = s_knu[tk];
@@ -372,6 +384,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
       for (int k = 1; k < 16; ++k) mx = fmaxf(mx, lv[k]);
       mx = fmaxf(mx, __shfl_xor(mx, 1));
       mx = fmaxf(mx, __shfl_xor(mx, 2));
+      mx = fmaxf(mx, __shfl_xor(mx, 4));
       // lazy max: raised only past m_run + kLazy (alpha = 1 otherwise)
       const bool grow = mx > m_run + kLazy;
       const float m_new = grow ? mx : m_run;
@@ -388,6 +401,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
       }
       ls += __shfl_xor(ls, 1);
       ls += __shfl_xor(ls, 2);
+      ls += __shfl_xor(ls, 4);
       l_run = l_run * alpha + ls;
       m_run = m_new;
       __syncthreads();   // every score is read: P may overwrite them
@@ -402,30 +416,23 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
     __syncthreads();
     const bool rescale = s_rescale != 0;
 
-    // ---- 5. o = alpha o + P x V for rows 32 mblk .., coordinate blocks cb0, cb0 + 1
+    // ---- 5. o = alpha o + P x V for rows 32 mblk .., coordinates 32 cb ..
     {
       if (rescale) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float al = s_alpha[32 * mblk + 8 * (r >> 2) + 4 * hi + (r & 3)];
-          o[0][r] *= al;
-          o[1][r] *= al;
-        }
+        for (int r = 0; r < 16; ++r) o[r] *= s_alpha[32 * mblk + 8 * (r >> 2) + 4 * hi + (r & 3)];
       }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < kTile / 16; ++ks) {
         const int prow = (32 * mblk + l32) * kPStride + 16 * ks + 8 * hi;
         const bf16x8 pa_h = *reinterpret_cast<const bf16x8 *>(&s_ph[prow]);
         const bf16x8 pa_l = *reinterpret_cast<const bf16x8 *>(&s_pl[prow]);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int vrow = (32 * (cb0 + c) + l32) * kVtStride + 16 * ks + 8 * hi;
-          const bf16x8 vb_h = *reinterpret_cast<const bf16x8 *>(&s_vth[vrow]);
-          const bf16x8 vb_l = *reinterpret_cast<const bf16x8 *>(&s_vtl[vrow]);
-          o[c] = mfma(pa_h, vb_h, o[c]);
-          o[c] = mfma(pa_h, vb_l, o[c]);
-          o[c] = mfma(pa_l, vb_h, o[c]);
-        }
+        const int vrow = (32 * cb + l32) * kVtStride + 16 * ks + 8 * hi;
+        const bf16x8 vb_h = *reinterpret_cast<const bf16x8 *>(&s_vth[vrow]);
+        const bf16x8 vb_l = *reinterpret_cast<const bf16x8 *>(&s_vtl[vrow]);
+        o = mfma(pa_h, vb_h, o);
+        o = mfma(pa_h, vb_l, o);
+        o = mfma(pa_l, vb_h, o);
       }
     }
   }
@@ -434,15 +441,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
   // (b, kv head, j), chunk), then head h
   const int nc = a.n_chunks;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 32 * mblk + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (m < rows_total) {
-        const int64_t grp = (static_cast<int64_t>(row_id) * a.n_new + m / g) * nc + chunk_id;
-        a.ws_part_o[(grp * g + m % g) * D + 32 * (cb0 + c) + l32] = o[c][r];
-      }
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + 32 * mblk + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (m < rows_total) {
+      const int64_t grp = (static_cast<int64_t>(row_id) * a.n_new + m / g) * nc + chunk_id;
+      a.ws_part_o[(grp * g + m % g) * D + 32 * cb + l32] = o[r];
     }
+  }
   if (sq == 0 && m0 + sm < rows_total) {
     const int m = m0 + sm;
     const int64_t grp = (static_cast<int64_t>(row_id) * a.n_new + m / g) * nc + chunk_id;
@@ -465,7 +470,7 @@ hipError_t launch_tiles(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
 
 DecodePlan plan_chunk_mfma(int batch, int n_q_heads, int n_kv_heads, int n_new, int64_t t_cap) {
   // ~256 work-groups over (b, kv head, 64-row block, token chunk); a chunk is
-  // whole 64-token tiles, at most kMaxDecodeChunks per row.
+  // whole tiles, at most kMaxDecodeChunks per row.
   DecodePlan p{};
   const int64_t g = n_q_heads / std::max(1, n_kv_heads);
   const int64_t n_mb = (g * n_new + kRows - 1) / kRows;
