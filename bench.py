@@ -37,9 +37,9 @@ HBM_PEAK_GBPS = 8000.0
 # --calib-copy 512, each scaled by the ratio of a 512 MiB device copy's known
 # bytes to what the same counter read for it.  Valid only for the encode
 # source they were taken on (sha256 below); otherwise reported as null.
-ENCODE_TRAFFIC = {"source_sha256": "78028214d8f86853d6c3476c48094b392f023f1bd6bc0fa53cbe35d5abc13f30",
+ENCODE_TRAFFIC = {"source_sha256": "c64c7410a72a51725ea1673f5416b2fde55896f452fa4f458b10631baa464d9a",
                   "workload": "llama3-8b-layer-b1-s32768",
-                  "fetch_bytes": 68477913, "write_bytes": 14682167}
+                  "fetch_bytes": 68486952, "write_bytes": 14684168}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attn HBM GB/s (% of peak) on compressed KV; encode Mvectors/s"
 
@@ -296,9 +296,25 @@ def chunk_only(T, kcb, vcb, caches, S, Hq, args, dev):
     end.record(stream)
     torch.cuda.synchronize()
     us = start.elapsed_time(end) * 1e3 / n
-    cache_bytes = B * kc0.codes.shape[1] * S * T.compressed_bytes_per_token(kcb, vcb)
-    return {"n_new": n_new, "us": round(us, 2), "queries_per_s": round(B * Hq * n_new / (us * 1e-6), 1),
-            "cache_bytes": cache_bytes, "cache_gbps_per_query_block": round(cache_bytes * n_new / (us * 1e-6) / 1e9, 1)}
+    Hkv = kc0.codes.shape[1]
+    cache_bytes = B * Hkv * S * T.compressed_bytes_per_token(kcb, vcb)
+    res = {"n_new": n_new, "us": round(us, 2), "queries_per_s": round(B * Hq * n_new / (us * 1e-6), 1),
+           "cache_bytes": cache_bytes}
+    g_ = Hq // Hkv
+    if T.api.chunk_uses_mfma(g_, n_new):
+        # per (query row, token): key dot (d), QJL dot (m) and value sum (d) multiply-adds; the kernel
+        # runs each fp32 product as 3 bf16 products (2 for the exact +-1 signs) over 64-row blocks
+        rows = g_ * n_new
+        blocks = -(-rows // 64)
+        m = kcb.qjl_dim
+        alg = 2.0 * B * Hkv * rows * S * (128 + m + 128)
+        issued = 2.0 * B * Hkv * blocks * 64 * S * (3 * 128 + 2 * m + 3 * 128)
+        res.update({"path": "mfma", "tflops_algorithmic": round(alg / (us * 1e-6) / 1e12, 1),
+                    "tflops_issued_bf16": round(issued / (us * 1e-6) / 1e12, 1),
+                    "frac_of_bf16_peak_issued": round(issued / (us * 1e-6) / 2.5e15, 4)})
+    else:
+        res["path"] = "decode kernel per query"
+    return res
 
 
 def append_steps(wl, kcb, vcb, up, steps, dev):
