@@ -1,9 +1,11 @@
 """tq_chunk_attention: a chunk of n_new queries per (b, q head), query j at
 position seq_len - n_new + j attending causally over the compressed cache.
 
-* Oracle parity (chunk_attention) at g = 1, 4, 8, n_new = 1, 5, 16, keys with
-  and without QJL, over ragged sequences, one shorter than the chunk (its
-  first queries see nothing and give zeros).
+* Oracle parity (chunk_attention) at g = 1, 2, 4, 8, n_new = 1 .. 24, keys
+  with and without QJL, bf16 and fp32 queries, over ragged sequences, one
+  shorter than the chunk (its first queries see nothing and give zeros); both
+  the decode-kernel path (< 16 query rows per kv head) and the matrix-core
+  path, including its padded row blocks (g = 1, 16 rows).
 * Query j equals tq_decode_attention of that query alone with
   seq_len - n_new + j + 1 tokens: bit for bit for n_new = 1 (same launch
   plan); within 1e-5 relative and absolute while fewer than 16 query rows per
@@ -51,20 +53,23 @@ def _per_query_decode(kcb, vcb, q, kc, vc, lens):
     return torch.stack(outs, dim=2)
 
 
-@pytest.mark.parametrize("kbits,m,vbits,g,n_new", [(2, 128, 3, 4, 5), (1, 128, 2, 8, 16), (3, 128, 4, 1, 1),
-                                                   (2, 0, 2, 4, 16), (4, 0, 3, 8, 5)])
-def test_chunk_parity(kbits, m, vbits, g, n_new):
+@pytest.mark.parametrize("kbits,m,vbits,g,n_new,qdt", [(2, 128, 3, 4, 5, "bf16"), (1, 128, 2, 8, 16, "bf16"),
+                                                       (3, 128, 4, 1, 1, "bf16"), (2, 0, 2, 4, 16, "bf16"),
+                                                       (4, 0, 3, 8, 5, "bf16"), (2, 128, 3, 1, 16, "f32"),
+                                                       (3, 128, 2, 2, 24, "f32"), (4, 128, 4, 2, 3, "f32")])
+def test_chunk_parity(kbits, m, vbits, g, n_new, qdt):
     B, Hkv, t_cap = 3, 2, 1100
     lens = [1100, 3, 640]
     Hq = Hkv * g
     rng = np.random.default_rng(1000 + 10 * kbits + g + n_new)
     k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap, lognormal_sigma=0.5))
     v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap, lognormal_sigma=0.5))
-    q = H.to_device(synth.bf16_bits(rng.standard_normal((B, Hq, n_new, 128)).astype(np.float32)), "bf16")
+    qf = rng.standard_normal((B, Hq, n_new, 128)).astype(np.float32)
+    q = H.to_device(synth.bf16_bits(qf), "bf16") if qdt == "bf16" else H.to_device(qf, "f32")
     kcb, vcb = H.gpu_book(kbits, m), H.gpu_book(vbits, 0)
     kc, vc = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, t_cap, t_cap)
     sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
-    _log(f"chunk kbits={kbits} m={m} vbits={vbits} g={g} n_new={n_new} lens={lens}")
+    _log(f"chunk kbits={kbits} m={m} vbits={vbits} g={g} n_new={n_new} q={qdt} lens={lens}")
     got = T.chunk_attention(kcb, vcb, q, kc, vc, sl)
     per = _per_query_decode(kcb, vcb, q, kc, vc, lens)
     torch.cuda.synchronize()

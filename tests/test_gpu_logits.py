@@ -66,7 +66,7 @@ def test_logits_parity(kbits, m, g):
 
 def test_logits_scale_and_seq_clamp():
     """softmax_scale scales every logit; seq_len beyond t_cap is clamped and
-    a negative one reads as empty."""
+    a negative one reads as empty; fp32 queries."""
     B, Hkv, g, t_cap = 3, 1, 4, 700
     rng = np.random.default_rng(9)
     k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap))
@@ -76,11 +76,16 @@ def test_logits_scale_and_seq_clamp():
     T.encode_into_cache(kcb, H.to_device(k.reshape(-1, 128), "bf16"), kc)
     sl = torch.tensor([10_000, -3, 333], dtype=torch.int32, device=H.DEV)
     got = T.attention_logits(kcb, q, kc, sl, logits=_nan_logits(B, Hkv * g, t_cap), softmax_scale=0.5)
+    # an fp32 query (values not representable in bf16)
+    q32 = torch.from_numpy(rng.standard_normal((B, Hkv * g, 128)).astype(np.float32)).to(H.DEV)
+    got32 = T.attention_logits(kcb, q32, kc, sl, logits=_nan_logits(B, Hkv * g, t_cap))
     torch.cuda.synchronize()
     seq_c = [t_cap, 0, 333]
     ref = H.oracle_logits(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), seq_c,
                           H.oracle_book(2, 128), g, scale=0.5)
     H.check_logits(got.cpu().numpy(), ref, seq_c)
+    ref32 = H.oracle_logits(q32.cpu().numpy().astype(np.float64), H.cache_to_host(kc), seq_c, H.oracle_book(2, 128), g)
+    H.check_logits(got32.cpu().numpy(), ref32, seq_c)
 
 
 def test_logits_llama8b_full():

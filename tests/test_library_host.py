@@ -135,3 +135,17 @@ def test_workspace_sizing():
         T.decode_workspace_bytes(0, 32, 8, 100)
     with pytest.raises(T.TQError):
         T.decode_workspace_bytes(1, 32, 8, 0)
+
+
+def test_chunk_workspace_sizing():
+    # one query per head: the decode plan; 16+ query rows per kv head: the
+    # matrix-core plan, which also holds (q~, s) of every query row
+    assert T.chunk_workspace_bytes(1, 32, 8, 1, 32768) == T.decode_workspace_bytes(1, 32, 8, 32768)
+    assert T.chunk_workspace_bytes(2, 32, 8, 3, 1000) == T.decode_workspace_bytes(6, 32, 8, 1000)
+    big = T.chunk_workspace_bytes(1, 32, 8, 16, 32768)
+    assert big % 256 == 0 and big >= 1 * 32 * 16 * 256 * 4
+    assert T.api.chunk_uses_mfma(4, 4) and not T.api.chunk_uses_mfma(4, 3)
+    with pytest.raises(T.TQError):
+        T.chunk_workspace_bytes(1, 32, 8, 0, 100)
+    with pytest.raises(T.TQError):
+        T.chunk_workspace_bytes(1, 30, 8, 4, 100)
