@@ -233,6 +233,33 @@ __device__ __forceinline__ void tab_load(const float *tab, int p, uint32_t n, fl
   }
 }
 
+// For g <= 4 an entry is 4 g bytes, so nibble n's scaled index n * 4 g fits in
+// a byte: two masks spread the 8 nibbles of a code word, already scaled, into
+// the bytes of two registers (even nibbles, odd nibbles), and one byte
+// extract per lookup remains.  o[k] = byte offset of nibble k's entry.
+template <int G>
+__device__ __forceinline__ void nibble_offsets(uint32_t w, uint32_t (&o)[8]) {
+  static_assert(G <= 4, "entries of g > 4 heads are 16-byte groups");
+  constexpr int S = G == 1 ? 2 : (G == 2 ? 3 : 4);   // log2 of the entry size in bytes
+  constexpr uint32_t M = 0x0F0F0F0Fu << S;
+  const uint32_t ev = (w << S) & M;
+  const uint32_t od = (S == 4) ? (w & M) : ((w >> (4 - S)) & M);
+  o[0] = ev & 0xFFu;
+  o[2] = __builtin_amdgcn_ubfe(ev, 8, 8);
+  o[4] = __builtin_amdgcn_ubfe(ev, 16, 8);
+  o[6] = ev >> 24;
+  o[1] = od & 0xFFu;
+  o[3] = __builtin_amdgcn_ubfe(od, 8, 8);
+  o[5] = __builtin_amdgcn_ubfe(od, 16, 8);
+  o[7] = od >> 24;
+}
+
+// tab_load for g <= 4 with the entry's byte offset within position p.
+template <int G>
+__device__ __forceinline__ void tab_load_off(const float *tab, int p, uint32_t off, float (&v)[G]) {
+  lds_load_g<G>(reinterpret_cast<const float *>(reinterpret_cast<const char *>(tab + p * 16 * G) + off), v);
+}
+
 // Entry index e of a table with P positions -> (p, n, h), the inverse of tab_offset.
 template <int G>
 __device__ __forceinline__ void tab_entry(int e, int &p, int &n, int &h) {
@@ -275,15 +302,27 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   constexpr int kJ = D / kParts;    // prologue: coordinates per partial dot product
   constexpr int kPass = 64 * kWaves;
   constexpr int KW = D * KB / 32;   // key code words per token
-  __shared__ float s_kdeq[KL::kEntries * KL::kCoords];
-  __shared__ float2 s_vdeq[SC ? 1 : 256];
-  // QJL sign table, entry (pos, nib, h) = sum_{k<4} s_h[4 pos + k] * (bit k of nib ? +1 : -1)
-  __shared__ float s_slut[QJL ? kSignLut * G : 1];
   using KT = KeyTab<KB, G>;
   constexpr int kFlight = G >= 8 ? 4 : 8;   // table positions read ahead (32 floats for g = 4, 8)
-  __shared__ float s_ktab[KT::kFloats];
-  __shared__ typename Lds<G>::Shared sh;
-  __shared__ float s_ml[kWaves][G][2];
+  // One block, tables first: every table lookup's address is then an index
+  // plus a constant below 64 KiB, which the LDS instruction's offset field
+  // holds (no add per lookup).
+  struct Smem {
+    alignas(16) float2 vdeq[SC ? 1 : 256];              // value pair table
+    alignas(16) float kdeq[KL::kEntries * KL::kCoords];  // key dequantization table
+    // QJL sign table, entry (pos, nib, h) = sum_{k<4} s_h[4 pos + k] * (bit k of nib ? +1 : -1)
+    alignas(16) float slut[QJL ? kSignLut * G : 1];
+    alignas(16) float ktab[KT::kFloats];                 // key-code tables (KeyTab)
+    alignas(16) typename Lds<G>::Shared sh;
+    alignas(16) float ml[kWaves][G][2];
+  };
+  __shared__ Smem smem;
+  float2 *const s_vdeq = smem.vdeq;
+  float *const s_kdeq = smem.kdeq;
+  float *const s_slut = smem.slut;
+  float *const s_ktab = smem.ktab;
+  typename Lds<G>::Shared &sh = smem.sh;
+  float (&s_ml)[kWaves][G][2] = smem.ml;
 
   const int chunk_id = blockIdx.x;
   const int hk = blockIdx.y / a.n_new;        // kv head
@@ -465,7 +504,25 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
       // q~ comes from scalar loads of the slot; the pointer is re-laundered
       // every few coordinates (depending on the products two groups back) so
       // that only two groups of scalar values are live: one in use, one in flight.
-      if constexpr (KT::kOn) {
+      if constexpr (KT::kOn && G <= 4) {
+        // one code word (8 positions) at a time: its word is made to depend
+        // on the sums so far, so only one word's reads are in flight
+#pragma unroll
+        for (int wi = 0; wi < KT::kPos / 8; ++wi) {
+          uint32_t w = kw[wi];
+#pragma unroll
+          for (int h = 0; h < G; ++h) asm volatile("" : "+v"(w) : "v"(dot[h]));
+          uint32_t o[8];
+          nibble_offsets<G>(w, o);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            float v[G];
+            tab_load_off<G>(s_ktab, 8 * wi + k, o[k], v);
+#pragma unroll
+            for (int h = 0; h < G; ++h) dot[h] += v[h];
+          }
+        }
+      } else if constexpr (KT::kOn) {
         uint32_t tab_off = 0;   // always 0; opaque so that only kFlight positions of reads are in flight
 #pragma unroll
         for (int p = 0; p < KT::kPos; ++p) {
@@ -523,18 +580,36 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
         float sd[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) sd[h] = 0.f;
-        uint32_t lut_off = 0;   // always 0; opaque so that only kFlight positions of reads are in flight
+        if constexpr (G <= 4) {
 #pragma unroll
-        for (int p = 0; p < 32; ++p) {
-          if ((p % kFlight) == 0) {
+          for (int wi = 0; wi < 4; ++wi) {
+            uint32_t w = sw[wi];
 #pragma unroll
-            for (int h = 0; h < G; ++h) asm volatile("" : "+v"(lut_off) : "v"(sd[h]));
+            for (int h = 0; h < G; ++h) asm volatile("" : "+v"(w) : "v"(sd[h]));
+            uint32_t o[8];
+            nibble_offsets<G>(w, o);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              float v[G];
+              tab_load_off<G>(s_slut, 8 * wi + k, o[k], v);
+#pragma unroll
+              for (int h = 0; h < G; ++h) sd[h] += v[h];
+            }
           }
-          const uint32_t nib = ((sw[p >> 3] >> (4 * (p & 7))) & 15u) + lut_off;
-          float v[G];
-          tab_load<G>(s_slut, p, nib, v);
+        } else {
+          uint32_t lut_off = 0;   // always 0; opaque so that only kFlight positions of reads are in flight
 #pragma unroll
-          for (int h = 0; h < G; ++h) sd[h] += v[h];
+          for (int p = 0; p < 32; ++p) {
+            if ((p % kFlight) == 0) {
+#pragma unroll
+              for (int h = 0; h < G; ++h) asm volatile("" : "+v"(lut_off) : "v"(sd[h]));
+            }
+            const uint32_t nib = ((sw[p >> 3] >> (4 * (p & 7))) & 15u) + lut_off;
+            float v[G];
+            tab_load<G>(s_slut, p, nib, v);
+#pragma unroll
+            for (int h = 0; h < G; ++h) sd[h] += v[h];
+          }
         }
         const float gq = a.qjl_coef * gamma;
 #pragma unroll
