@@ -217,30 +217,47 @@ __device__ __forceinline__ int tab_offset(int p, int n, int h) {
   return ((p * (G / 4) + h / 4) * 16 + n) * 4 + (h & 3);
 }
 
-template <int G>
-__device__ __forceinline__ void tab_load(const float *tab, int p, uint32_t n, float (&v)[G]) {
-  if constexpr (G <= 4) {
-    lds_load_g<G>(tab + (p * 16 + n) * G, v);
+// Ordering without instructions: x is made to depend on the g values d, so
+// whatever uses x waits for them.  One asm statement per call: the compiler
+// separates consecutive inline-asm statements with s_nop.
+template <int G, typename T>
+__device__ __forceinline__ void depend_v(T &x, const float (&d)[G]) {
+  if constexpr (G == 1) {
+    asm volatile("" : "+v"(x) : "v"(d[0]));
+  } else if constexpr (G == 2) {
+    asm volatile("" : "+v"(x) : "v"(d[0]), "v"(d[1]));
+  } else if constexpr (G == 4) {
+    asm volatile("" : "+v"(x) : "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]));
   } else {
-#pragma unroll
-    for (int q4 = 0; q4 < G / 4; ++q4) {
-      const float4 t = reinterpret_cast<const float4 *>(tab + (p * (G / 4) + q4) * 64)[n];
-      v[4 * q4] = t.x;
-      v[4 * q4 + 1] = t.y;
-      v[4 * q4 + 2] = t.z;
-      v[4 * q4 + 3] = t.w;
-    }
+    asm volatile("" : "+v"(x) : "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]), "v"(d[4]), "v"(d[5]), "v"(d[6]), "v"(d[7]));
+  }
+}
+// four values at once (g = 8 table reads, four positions in flight)
+__device__ __forceinline__ void depend4_v(uint32_t *o, const float (&d)[8]) {
+  asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3])
+               : "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]), "v"(d[4]), "v"(d[5]), "v"(d[6]), "v"(d[7]));
+}
+template <int G, typename T>
+__device__ __forceinline__ void depend_s(T &x, const float (&d)[G]) {
+  if constexpr (G == 1) {
+    asm volatile("" : "+s"(x) : "v"(d[0]));
+  } else if constexpr (G == 2) {
+    asm volatile("" : "+s"(x) : "v"(d[0]), "v"(d[1]));
+  } else if constexpr (G == 4) {
+    asm volatile("" : "+s"(x) : "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]));
+  } else {
+    asm volatile("" : "+s"(x) : "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]), "v"(d[4]), "v"(d[5]), "v"(d[6]), "v"(d[7]));
   }
 }
 
-// For g <= 4 an entry is 4 g bytes, so nibble n's scaled index n * 4 g fits in
-// a byte: two masks spread the 8 nibbles of a code word, already scaled, into
+// Nibble n's entry starts n * 4 g bytes into its position for g <= 4, and
+// n * 16 bytes into each 4-head group for g = 8: the scaled index fits in a
+// byte.  Two masks spread the 8 nibbles of a code word, already scaled, into
 // the bytes of two registers (even nibbles, odd nibbles), and one byte
 // extract per lookup remains.  o[k] = byte offset of nibble k's entry.
 template <int G>
 __device__ __forceinline__ void nibble_offsets(uint32_t w, uint32_t (&o)[8]) {
-  static_assert(G <= 4, "entries of g > 4 heads are 16-byte groups");
-  constexpr int S = G == 1 ? 2 : (G == 2 ? 3 : 4);   // log2 of the entry size in bytes
+  constexpr int S = G == 1 ? 2 : (G == 2 ? 3 : 4);   // log2 of the entry (group) size in bytes
   constexpr uint32_t M = 0x0F0F0F0Fu << S;
   const uint32_t ev = (w << S) & M;
   const uint32_t od = (S == 4) ? (w & M) : ((w >> (4 - S)) & M);
@@ -254,10 +271,21 @@ __device__ __forceinline__ void nibble_offsets(uint32_t w, uint32_t (&o)[8]) {
   o[7] = od >> 24;
 }
 
-// tab_load for g <= 4 with the entry's byte offset within position p.
+// tab_load with the entry's byte offset (nibble_offsets) within position p.
 template <int G>
 __device__ __forceinline__ void tab_load_off(const float *tab, int p, uint32_t off, float (&v)[G]) {
-  lds_load_g<G>(reinterpret_cast<const float *>(reinterpret_cast<const char *>(tab + p * 16 * G) + off), v);
+  if constexpr (G <= 4) {
+    lds_load_g<G>(reinterpret_cast<const float *>(reinterpret_cast<const char *>(tab + p * 16 * G) + off), v);
+  } else {
+#pragma unroll
+    for (int q4 = 0; q4 < G / 4; ++q4) {
+      const float4 t = *reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(tab + (p * (G / 4) + q4) * 64) + off);
+      v[4 * q4] = t.x;
+      v[4 * q4 + 1] = t.y;
+      v[4 * q4 + 2] = t.z;
+      v[4 * q4 + 3] = t.w;
+    }
+  }
 }
 
 // Entry index e of a table with P positions -> (p, n, h), the inverse of tab_offset.
@@ -510,8 +538,7 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
 #pragma unroll
         for (int wi = 0; wi < KT::kPos / 8; ++wi) {
           uint32_t w = kw[wi];
-#pragma unroll
-          for (int h = 0; h < G; ++h) asm volatile("" : "+v"(w) : "v"(dot[h]));
+          depend_v<G>(w, dot);
           uint32_t o[8];
           nibble_offsets<G>(w, o);
 #pragma unroll
@@ -523,18 +550,23 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
           }
         }
       } else if constexpr (KT::kOn) {
-        uint32_t tab_off = 0;   // always 0; opaque so that only kFlight positions of reads are in flight
+        // g = 8: kFlight positions' reads in flight, their offsets made to
+        // depend on the sums so far
 #pragma unroll
-        for (int p = 0; p < KT::kPos; ++p) {
-          if ((p % kFlight) == 0) {
+        for (int wi = 0; wi < KT::kPos / 8; ++wi) {
+          uint32_t o[8];
+          nibble_offsets<G>(kw[wi], o);
 #pragma unroll
-            for (int h = 0; h < G; ++h) asm volatile("" : "+v"(tab_off) : "v"(dot[h]));
+          for (int k = 0; k < 8; ++k) {
+            if constexpr (G == 8) {
+              static_assert(kFlight == 4, "g = 8 keeps four positions in flight");
+              if ((k % 4) == 0) depend4_v(&o[k], dot);
+            }
+            float v[G];
+            tab_load_off<G>(s_ktab, 8 * wi + k, o[k], v);
+#pragma unroll
+            for (int h = 0; h < G; ++h) dot[h] += v[h];
           }
-          const uint32_t nib = ((kw[p >> 3] >> (4 * (p & 7))) & 15u) + tab_off;
-          float v[G];
-          tab_load<G>(s_ktab, p, nib, v);
-#pragma unroll
-          for (int h = 0; h < G; ++h) dot[h] += v[h];
         }
       }
       uniform_fptr qv = qs;
@@ -543,8 +575,7 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
       for (int g = 0; g < (KT::kOn ? 0 : KL::kLookups); ++g) {
         const int c0 = g * KL::kCoords;
         if ((c0 % kRelaunder) == 0) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) asm volatile("" : "+s"(qv) : "v"(snap[h]));
+          depend_s<G>(qv, snap);
 #pragma unroll
           for (int h = 0; h < G; ++h) snap[h] = dot[h];
         }
@@ -580,33 +611,19 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
         float sd[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) sd[h] = 0.f;
-        if constexpr (G <= 4) {
 #pragma unroll
-          for (int wi = 0; wi < 4; ++wi) {
-            uint32_t w = sw[wi];
+        for (int wi = 0; wi < 4; ++wi) {
+          uint32_t w = sw[wi];
+          if constexpr (G <= 4) depend_v<G>(w, sd);
+          uint32_t o[8];
+          nibble_offsets<G>(w, o);
 #pragma unroll
-            for (int h = 0; h < G; ++h) asm volatile("" : "+v"(w) : "v"(sd[h]));
-            uint32_t o[8];
-            nibble_offsets<G>(w, o);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              float v[G];
-              tab_load_off<G>(s_slut, 8 * wi + k, o[k], v);
-#pragma unroll
-              for (int h = 0; h < G; ++h) sd[h] += v[h];
+          for (int k = 0; k < 8; ++k) {
+            if constexpr (G == 8) {
+              if ((k % 4) == 0) depend4_v(&o[k], sd);
             }
-          }
-        } else {
-          uint32_t lut_off = 0;   // always 0; opaque so that only kFlight positions of reads are in flight
-#pragma unroll
-          for (int p = 0; p < 32; ++p) {
-            if ((p % kFlight) == 0) {
-#pragma unroll
-              for (int h = 0; h < G; ++h) asm volatile("" : "+v"(lut_off) : "v"(sd[h]));
-            }
-            const uint32_t nib = ((sw[p >> 3] >> (4 * (p & 7))) & 15u) + lut_off;
             float v[G];
-            tab_load<G>(s_slut, p, nib, v);
+            tab_load_off<G>(s_slut, 8 * wi + k, o[k], v);
 #pragma unroll
             for (int h = 0; h < G; ++h) sd[h] += v[h];
           }
