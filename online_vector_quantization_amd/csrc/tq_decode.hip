@@ -13,7 +13,7 @@
 // [same memory-wall article, section 1]: decode is memory-bound, so the kernel
 // streams the packed codes once and keeps everything else on chip.
 //
-// Work-group = (batch b, kv head, chunk of tokens), 8 waves:
+// Work-group = (batch b, kv head [x query of a chunk], chunk of tokens), 8 waves:
 //  0. prologue: q~ = Pi_k q and s = S q~ = (S Pi_k) q for the g q heads of
 //     this kv head (parallel partial dot products reduced in LDS, all their
 //     global reads issued at once); q~ goes to a per-group workspace slot so
@@ -21,10 +21,12 @@
 //     table of signed partial sums of s, a key dequantization table and a
 //     value pair table are built in LDS.
 //  1. each wave, per 64-token tile:
-//     * scores, one token per lane: key codes dequantized through the LDS
-//       table (one lookup per code byte) times q~ from scalar registers; the
-//       sign term is a sum of table lookups, each giving 4 signs' partial sum
-//       for all g heads at once;
+//     * scores, one token per lane: for 1- and 2-bit codes and g >= 2 a sum
+//       of table lookups, one per code nibble, each giving that nibble's
+//       partial dot product for all g heads; otherwise key codes dequantized
+//       through an LDS table times q~ from scalar registers; the sign term is
+//       a sum of table lookups, each giving 4 signs' partial sum for all g
+//       heads at once;
 //     * online softmax with a lazily raised running max;
 //     * value sum: the tile's weights and value records are staged in LDS
 //       (records read as one coalesced block); lane (token group, coordinate
@@ -34,6 +36,12 @@
 //     workspace.
 // A second, small launch merges the chunks of each (b, q head) (log-sum-exp),
 // applies Pi_v^T and writes the output.
+//
+// The same kernel serves two more calls: with SC (scores only) it ends after
+// the key phase of each tile and writes every l_t (no values, no merge, no
+// second launch); with n_new > 1 queries per (b, q head) the grid's y
+// dimension also runs over the query j, whose causal window
+// seq_len - n_new + j + 1 is uniform across the work-group.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
