@@ -90,35 +90,44 @@ __device__ __forceinline__ float load_query(const void *q, int q_bf16, int64_t i
   return static_cast<const float *>(q)[idx];
 }
 
-// q~ = Pi_k q and s = (S Pi_k) q of one query row per work-group, written to
-// row ((b Hkv + hk) n_new + j) g + h of the prep buffer.
-template <bool QJL>
+// q~ = Pi_k q and s = (S Pi_k) q of the g query rows of one (b, kv head, j)
+// per work-group, written to rows ((b Hkv + hk) n_new + j) g + h of the prep
+// buffer.  Thread i < d holds column i of Pi_k^T, thread d + i column i of
+// (S Pi_k)^T (all reads issued before the first product), and takes the dot
+// products of all g queries: each matrix is read once per g rows.
+template <bool QJL, int G>
 __global__ __launch_bounds__(2 * D) void qprep_kernel(DecodeArgs a) {
-  __shared__ float sq[D];
-  const int qi = blockIdx.x;
-  const int g = a.n_q_heads / a.n_kv_heads;
-  const int h = qi % g;
-  const int j = (qi / g) % a.n_new;
-  const int bhk = qi / g / a.n_new;
+  __shared__ float sq[G][D];
+  const int qrow = blockIdx.x;   // (b Hkv + hk) n_new + j
+  const int j = qrow % a.n_new;
+  const int bhk = qrow / a.n_new;
   const int b = bhk / a.n_kv_heads, hk = bhk % a.n_kv_heads;
   const int tid = threadIdx.x;
-  if (tid < D)
-    sq[tid] = load_query(a.q, a.q_bf16, (static_cast<int64_t>(b * a.n_q_heads + hk * g + h) * a.n_new + j) * D + tid);
-  __syncthreads();
-  // every matrix read is issued before the first product: one round trip
+  for (int e = tid; e < G * D; e += 2 * D)
+    sq[e / D][e % D] =
+        load_query(a.q, a.q_bf16, (static_cast<int64_t>(b * a.n_q_heads + hk * G + e / D) * a.n_new + j) * D + e % D);
   const int i = tid & (D - 1);
   const float *mat = tid < D ? a.rot_k_t : a.qjl_rot_t;
-  float acc = 0.f;
+  float acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.f;
   if (tid < D || QJL) {
     float col[D];
 #pragma unroll
     for (int jj = 0; jj < D; ++jj) col[jj] = mat[jj * D + i];
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
 #pragma unroll
-    for (int jj = 0; jj < D; ++jj) part[jj & 3] = fmaf(col[jj], sq[jj], part[jj & 3]);
-    acc = (part[0] + part[1]) + (part[2] + part[3]);
+    for (int h = 0; h < G; ++h) {
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < D; ++jj) part[jj & 3] = fmaf(col[jj], sq[h][jj], part[jj & 3]);
+      acc[h] = (part[0] + part[1]) + (part[2] + part[3]);
+    }
+  } else {
+    __syncthreads();
   }
-  a.ws_qprep[static_cast<int64_t>(qi) * kQpStride + tid] = acc;
+#pragma unroll
+  for (int h = 0; h < G; ++h) a.ws_qprep[(static_cast<int64_t>(qrow) * G + h) * kQpStride + tid] = acc[h];
 }
 
 template <int KB, bool QJL>
@@ -497,11 +506,19 @@ hipError_t launch_chunk_mfma(const DecodeArgs &a, hipStream_t stream) {
   if (a.n_chunks > kMaxDecodeChunks || a.v_bits < 1 || a.v_bits > 4 || a.n_new < 1 ||
       static_cast<int64_t>(a.n_kv_heads) * n_mb > 65535 || a.ws_qprep == nullptr)
     return hipErrorInvalidValue;
-  const int n_rows = a.batch * a.n_q_heads * a.n_new;
-  if (a.qjl_m > 0) {
-    hipLaunchKernelGGL(qprep_kernel<true>, dim3(n_rows), dim3(2 * D), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(qprep_kernel<false>, dim3(n_rows), dim3(2 * D), 0, stream, a);
+  const int n_qrows = a.batch * a.n_kv_heads * a.n_new;   // (b, kv head, j)
+  const bool qjl = a.qjl_m > 0;
+  switch (g) {
+#define TQ_QP(GG)                                                                                   \
+  case GG:                                                                                          \
+    if (qjl)                                                                                        \
+      hipLaunchKernelGGL((qprep_kernel<true, GG>), dim3(n_qrows), dim3(2 * D), 0, stream, a);      \
+    else                                                                                            \
+      hipLaunchKernelGGL((qprep_kernel<false, GG>), dim3(n_qrows), dim3(2 * D), 0, stream, a);     \
+    break;
+    TQ_QP(1) TQ_QP(2) TQ_QP(4) TQ_QP(8)
+#undef TQ_QP
+    default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
