@@ -506,8 +506,17 @@ tq_status tq_append_decode(const tq_codebook *kcb, const tq_codebook *vcb, const
   }
   da.seq_add = 1;
   da.seq_inc = seq_len;
-  if ((st = run_encode(kcb, ka, kv_dtype == TQ_F32, stream)) != TQ_OK) return st;
-  if ((st = run_encode(vcb, va, kv_dtype == TQ_F32, stream)) != TQ_OK) return st;
+  if (kv_dtype == TQ_BF16) {
+    // keys and values side by side in one launch
+    DeviceGuard guard(kcb->device);
+    if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
+    const hipError_t e = tq::launch_encode_pair(ka, kcb->host.bits, kcb->host.m > 0, va, vcb->host.bits,
+                                                cu_count(kcb->device), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "append encode launch: %s", hipGetErrorString(e));
+  } else {
+    if ((st = run_encode(kcb, ka, true, stream)) != TQ_OK) return st;
+    if ((st = run_encode(vcb, va, true, stream)) != TQ_OK) return st;
+  }
   return run_decode(kcb, da, stream);
 }
 

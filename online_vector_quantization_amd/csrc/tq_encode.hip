@@ -123,6 +123,21 @@ __device__ __forceinline__ int64_t dest_row(const EncodeArgs &a, int64_t vec, bo
   return vec;
 }
 
+// The encode of work-group `block` of `nblocks` over the rows of `a`;
+// s_frag holds (QJL ? 4 : 2) fragment splits, s_qlut the cell table.
+template <int BITS, bool QJL, bool XF32, bool DBG>
+__device__ __forceinline__ void encode_body(const EncodeArgs &a, uint4 *s_frag, float4 *s_qlut, int block,
+                                            int nblocks) {
+  constexpr int NT = kNT;
+  constexpr int kWaves = EncGeom<QJL>::kWaves;
+  constexpr int kThreads = EncGeom<QJL>::kThreads;
+#define TQ_ENC_BLOCK block
+#define TQ_ENC_NBLOCKS nblocks
+#include "tq_encode_body.inc"
+#undef TQ_ENC_BLOCK
+#undef TQ_ENC_NBLOCKS
+}
+
 template <int BITS, bool QJL, bool XF32, bool DBG>
 __global__ __launch_bounds__(EncGeom<QJL>::kThreads) void encode_kernel(EncodeArgs a) {
   constexpr int NT = kNT;
@@ -131,255 +146,56 @@ __global__ __launch_bounds__(EncGeom<QJL>::kThreads) void encode_kernel(EncodeAr
   __shared__ uint4 s_frag[(QJL ? 4 : 2) * kFragU4];
   __shared__ float4 s_qlut[kQuantCellEntries];
 
-  const int tid = threadIdx.x;
-  for (int i = tid; i < 2 * kFragU4; i += kThreads) s_frag[i] = a.frag_rot[i];
-  if constexpr (QJL) {
-    for (int i = tid; i < 2 * kFragU4; i += kThreads) s_frag[2 * kFragU4 + i] = a.frag_qjl[i];
+#define TQ_ENC_BLOCK blockIdx.x
+#define TQ_ENC_NBLOCKS gridDim.x
+#include "tq_encode_body.inc"
+#undef TQ_ENC_BLOCK
+#undef TQ_ENC_NBLOCKS
+}
+
+// A decode-loop step's keys and values in one launch: work-groups
+// 0 .. k_blocks - 1 encode the key rows (ka), the rest the value rows (va),
+// sharing one LDS block sized for the keys' four fragment splits.  bf16 input.
+template <int KBITS, bool KQJL, int VBITS>
+__global__ __launch_bounds__(EncGeom<true>::kThreads) void encode_pair_kernel(EncodeArgs ka, EncodeArgs va,
+                                                                              int k_blocks) {
+  static_assert(EncGeom<true>::kThreads == EncGeom<false>::kThreads, "one work-group size for both");
+  __shared__ uint4 s_frag[4 * kFragU4];
+  __shared__ float4 s_qlut[kQuantCellEntries];
+  if (static_cast<int>(blockIdx.x) < k_blocks) {
+    encode_body<KBITS, KQJL, false, false>(ka, s_frag, s_qlut, blockIdx.x, k_blocks);
+  } else {
+    encode_body<VBITS, false, false, false>(va, s_frag, s_qlut, blockIdx.x - k_blocks, gridDim.x - k_blocks);
   }
-  for (int i = tid; i < kQuantCellEntries; i += kThreads) s_qlut[i] = a.qlut[i];
-  __syncthreads();
+}
 
+// Work-groups of an encode of a.n rows.
+int encode_grid(const EncodeArgs &a, bool qjl, int num_cus) {
+  const int64_t tiles = (a.n + 16 * kNT - 1) / (16 * kNT);
+  constexpr int kWaves = EncGeom<true>::kWaves;
+  const int64_t wgs = (tiles + kWaves - 1) / kWaves;
+  // Keys need the Pi and S fragments (128 KiB of LDS): one work-group per CU;
+  // values need only Pi's (64 KiB) and fewer registers: two per CU.
+  const int per_cu = qjl ? 1 : 2;
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(wgs, static_cast<int64_t>(num_cus) * per_cu)));
+}
 
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int j = lane & 15;
-  // Per-lane fragment indices for the Pi and S halves of LDS, opaque to the
-  // compiler: every fragment read is then one base register plus an
-  // immediate offset (S's half lies beyond the 64 KiB immediate range of
-  // the s_frag base, which otherwise costs a register per fragment).
-  uint32_t rot_l = lane, qjl_l = lane + 2 * kFragU4;
-  asm volatile("" : "+v"(rot_l), "+v"(qjl_l));
-  const int kk = lane >> 4;
-  const int64_t n = a.n;
-  const int64_t tiles = (n + 16 * NT - 1) / (16 * NT);
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
-  const float qscale = a.qscale, qbias = a.qbias;
-
-  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + wave; tile < tiles; tile += stride) {
-    XRegs<XF32> cur[NT];
-    load_x<XF32, NT>(a, tile, j, kk, cur);
-
-    bf16x8 bx[NT][4];
-    bf16x8 bxlo[XF32 ? NT : 1][4];
-    float nu[NT], inv[NT];
-
-    // ---- B operands and norms
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float ss = 0.f;
-      if constexpr (!XF32) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint4 w = cur[nt].w[s];
-          bx[nt][s] = u4_as_bf16(w);
-          // x_i^2 summed two at a time (bf16 products are exact in fp32)
-          ss = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(w.x), u32_as_bf16x2(w.x), ss, false);
-          ss = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(w.y), u32_as_bf16x2(w.y), ss, false);
-          ss = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(w.z), u32_as_bf16x2(w.z), ss, false);
-          ss = __builtin_amdgcn_fdot2_f32_bf16(u32_as_bf16x2(w.w), u32_as_bf16x2(w.w), ss, false);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float4 p0 = cur[nt].w[2 * s], p1 = cur[nt].w[2 * s + 1];
-          const f32x8 v = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-          split_bf16(v, bx[nt][s], bxlo[nt][s]);
-        }
-      }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      nu[nt] = sqrtf(ss);
-      inv[nt] = (nu[nt] == 0.f) ? 0.f : 1.f / nu[nt];
-    }
-
-    int64_t vec[NT];
-    bool valid[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      vec[nt] = tile * (16 * NT) + nt * 16 + j;
-      valid[nt] = vec[nt] < n;
-    }
-
-    // Output block t of y = Pi x (M = output coordinate, N = vector, K = input
-    // coordinate) gives the lane y[32 kk + 4 t + e] of vector vec[nt].
-    auto rotate_block = [&](int t, f32x4 (&acc)[NT]) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 ah = u4_as_bf16(s_frag[rot_l + (t * 4 + s) * 64]);
-        const bf16x8 al = u4_as_bf16(s_frag[rot_l + kFragU4 + (t * 4 + s) * 64]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma(ah, bx[nt][s], acc[nt]);
-        if constexpr (XF32) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma(ah, bxlo[nt][s], acc[nt]);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma(al, bx[nt][s], acc[nt]);
-      }
-    };
-
-    uint32_t words[NT][BITS];
-    float rr[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      rr[nt] = 0.f;
-#pragma unroll
-      for (int w = 0; w < BITS; ++w) words[nt][w] = 0u;
-    }
-    // Quantize, residual and pack of block t; the residual goes to rv.
-    auto quantize_block = [&](int t, f32x4 (&acc)[NT], float (&rv)[NT][4]) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float y = acc[nt][e] * inv[nt];
-          // cell of y: q.x counts the thresholds below the cell; q.y is the only
-          // threshold that may lie in the cell (NaN when none); q.z / q.w are the
-          // centroids below / above it.
-          // |y| <= 1 up to rounding gives cells 0 .. kQuantCells; the clamp only
-          // matters for inputs whose norm is lost to underflow
-          const uint32_t cell = min(__float2uint_rz(fmaf(y, qscale, qbias)), static_cast<uint32_t>(kQuantCellEntries - 1));
-          const float4 q = s_qlut[cell];
-          const bool up = y >= q.y;
-          const uint32_t idx = __float_as_uint(q.x) + (up ? 1u : 0u);
-          const int pos = (4 * t + e) * BITS;
-          words[nt][pos / 32] |= idx << (pos % 32);
-          if ((pos % 32) + BITS > 32) words[nt][pos / 32 + 1] |= idx >> (32 - (pos % 32));
-          if constexpr (QJL) {
-            const float r = y - (up ? q.w : q.z);
-            rr[nt] = fmaf(r, r, rr[nt]);
-            rv[nt][e] = r;
-          }
-          if constexpr (DBG) acc[nt][e] = y;
-        }
-        if constexpr (DBG) {
-          if (a.dbg_rot != nullptr && valid[nt])
-            *reinterpret_cast<float4 *>(a.dbg_rot + vec[nt] * kHeadDim + 32 * kk + 4 * t) =
-                make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
-        }
-        // materialize the packed words now: otherwise the compiler sinks the
-        // packing into the final (conditional) store and keeps every
-        // coordinate's operands live until then
-#pragma unroll
-        for (int w = 0; w < BITS; ++w) asm volatile("" : "+v"(words[nt][w]));
-        if constexpr (QJL) asm volatile("" : "+v"(rr[nt]));
-      }
-    };
-
-    // QJL k-step s takes rotated coordinates 32 kk + 8 s .. + 7 of the lane,
-    // i.e. blocks 2 s and 2 s + 1: their residuals, split into bf16 hi and lo.
-    f32x4 pacc[QJL ? 8 : 1][NT];
-    if constexpr (QJL) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) pacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    auto qjl_step = [&](int s, const bf16x8 (&rh)[NT], const bf16x8 (&rl)[NT]) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bf16x8 sh = u4_as_bf16(s_frag[qjl_l + (t * 4 + s) * 64]);
-        const bf16x8 sl = u4_as_bf16(s_frag[qjl_l + kFragU4 + (t * 4 + s) * 64]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) pacc[t][nt] = mfma(sh, rh[nt], pacc[t][nt]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) pacc[t][nt] = mfma(sh, rl[nt], pacc[t][nt]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) pacc[t][nt] = mfma(sl, rh[nt], pacc[t][nt]);
-      }
-    };
-
-    // ---- software pipeline over the 8 output blocks: step t quantizes block t
-    // (vector work) while the MFMAs of block t + 1 and, on even steps, of the
-    // QJL k-step whose residual pair was completed on the step before
-    // (independent of it) execute.
-    f32x4 racc[2][NT];
-    bf16x8 rh[QJL ? NT : 1], rl[QJL ? NT : 1];
-    float rpend[QJL ? NT : 1][4];
-    rotate_block(0, racc[0]);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (t < 7) rotate_block(t + 1, racc[(t + 1) & 1]);
-      if constexpr (QJL) {
-        if (t >= 2 && (t & 1) == 0) qjl_step(t / 2 - 1, rh, rl);
-      }
-      float rv[NT][4];
-      quantize_block(t, racc[t & 1], rv);
-      if constexpr (QJL) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if ((t & 1) == 0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rpend[nt][e] = rv[nt][e];
-          } else {
-            const f32x8 v = {rpend[nt][0], rpend[nt][1], rpend[nt][2], rpend[nt][3], rv[nt][0], rv[nt][1], rv[nt][2], rv[nt][3]};
-            split_bf16(v, rh[nt], rl[nt]);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (QJL) qjl_step(3, rh, rl);
-
-    // ---- emit codes, norms, residual norms
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int64_t row = dest_row(a, vec[nt], valid[nt]);
-      const bool ok = valid[nt] && row >= 0 && row < a.cache_rows;
-      if constexpr (QJL) {
-        rr[nt] += __shfl_xor(rr[nt], 16);
-        rr[nt] += __shfl_xor(rr[nt], 32);
-      }
-      if (ok) {
-        uint32_t *cp = a.codes + row * (4 * BITS) + kk * BITS;
-        if constexpr (BITS == 4) {
-          *reinterpret_cast<uint4 *>(cp) = make_uint4(words[nt][0], words[nt][1], words[nt][2], words[nt][3]);
-        } else if constexpr (BITS == 2) {
-          *reinterpret_cast<uint2 *>(cp) = make_uint2(words[nt][0], words[nt][1]);
-        } else {
-#pragma unroll
-          for (int w = 0; w < BITS; ++w) cp[w] = words[nt][w];
-        }
-        if (kk == 0) {
-          a.norms[row] = nu[nt];
-          if constexpr (QJL) a.res_norms[row] = sqrtf(rr[nt]);
-        }
-      }
-      if constexpr (QJL) {
-        // sign word bit (4 t + e) = [p > 0], built most significant bit first
-        uint32_t sw = 0u;
-#pragma unroll
-        for (int t = 7; t >= 0; --t)
-#pragma unroll
-          for (int e = 3; e >= 0; --e) sw = shift_in_positive(sw, pacc[t][nt][e]);
-        if constexpr (DBG) {
-          if (a.dbg_proj != nullptr && valid[nt]) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-              *reinterpret_cast<float4 *>(a.dbg_proj + vec[nt] * kQjlDim + 32 * kk + 4 * t) =
-                  make_float4(pacc[t][nt][0], pacc[t][nt][1], pacc[t][nt][2], pacc[t][nt][3]);
-          }
-        }
-        if (ok) a.signs[row * (kQjlDim / 32) + kk] = sw;
-      }
-    }
+template <int KBITS, bool KQJL>
+hipError_t launch_pair_k(const EncodeArgs &ka, const EncodeArgs &va, int vbits, int kb, int vb, hipStream_t stream) {
+  const dim3 grid(kb + vb), block(EncGeom<true>::kThreads);
+  switch (vbits) {
+    case 1: hipLaunchKernelGGL((encode_pair_kernel<KBITS, KQJL, 1>), grid, block, 0, stream, ka, va, kb); break;
+    case 2: hipLaunchKernelGGL((encode_pair_kernel<KBITS, KQJL, 2>), grid, block, 0, stream, ka, va, kb); break;
+    case 3: hipLaunchKernelGGL((encode_pair_kernel<KBITS, KQJL, 3>), grid, block, 0, stream, ka, va, kb); break;
+    case 4: hipLaunchKernelGGL((encode_pair_kernel<KBITS, KQJL, 4>), grid, block, 0, stream, ka, va, kb); break;
+    default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 template <int BITS, bool QJL, bool XF32>
 hipError_t launch_t(const EncodeArgs &a, int num_cus, hipStream_t stream) {
-  const int64_t tiles = (a.n + 16 * kNT - 1) / (16 * kNT);
-  constexpr int kWaves = EncGeom<QJL>::kWaves;
-  const int64_t wgs = (tiles + kWaves - 1) / kWaves;
-  // Keys need the Pi and S fragments (128 KiB of LDS): one work-group per CU;
-  // values need only Pi's (64 KiB) and fewer registers: two per CU.
-  const int per_cu = QJL ? 1 : 2;
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(wgs, static_cast<int64_t>(num_cus) * per_cu)));
+  const int grid = encode_grid(a, QJL, num_cus);
   if (a.dbg_rot != nullptr || a.dbg_proj != nullptr)
     hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, true>), dim3(grid), dim3(EncGeom<QJL>::kThreads), 0, stream, a);
   else
@@ -450,6 +266,23 @@ bool build_quant_cells(const float *thresholds, const float *centroids, int leve
   *qscale = static_cast<float>(kQuantCells / 2.0);
   *qbias = static_cast<float>(kQuantCells / 2.0);
   return true;
+}
+
+hipError_t launch_encode_pair(const EncodeArgs &ka, int kbits, bool kqjl, const EncodeArgs &va, int vbits,
+                              int num_cus, hipStream_t stream) {
+  if (ka.dbg_rot != nullptr || ka.dbg_proj != nullptr || va.dbg_rot != nullptr) return hipErrorInvalidValue;
+  const int kb = encode_grid(ka, kqjl, num_cus), vb = encode_grid(va, false, num_cus);
+  switch (kbits * 2 + (kqjl ? 1 : 0)) {
+    case 2: return launch_pair_k<1, false>(ka, va, vbits, kb, vb, stream);
+    case 3: return launch_pair_k<1, true>(ka, va, vbits, kb, vb, stream);
+    case 4: return launch_pair_k<2, false>(ka, va, vbits, kb, vb, stream);
+    case 5: return launch_pair_k<2, true>(ka, va, vbits, kb, vb, stream);
+    case 6: return launch_pair_k<3, false>(ka, va, vbits, kb, vb, stream);
+    case 7: return launch_pair_k<3, true>(ka, va, vbits, kb, vb, stream);
+    case 8: return launch_pair_k<4, false>(ka, va, vbits, kb, vb, stream);
+    case 9: return launch_pair_k<4, true>(ka, va, vbits, kb, vb, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_encode(const EncodeArgs &a, int bits, bool qjl, bool x_f32, int num_cus,

@@ -59,6 +59,9 @@ bool build_quant_cells(const float *thresholds, const float *centroids, int leve
 // Enqueues the encode kernel; returns the launch error (hipSuccess on success).
 hipError_t launch_encode(const EncodeArgs &a, int bits, bool qjl, bool x_f32, int num_cus,
                          hipStream_t stream);
+// Keys (ka) and values (va, no QJL) of bf16 rows in one launch, no debug outputs.
+hipError_t launch_encode_pair(const EncodeArgs &ka, int kbits, bool kqjl, const EncodeArgs &va, int vbits,
+                              int num_cus, hipStream_t stream);
 
 constexpr int kMaxDecodeChunks = 128;   // chunks per (batch, kv head)
 
