@@ -36,7 +36,8 @@ HBM_PEAK_GBPS = 8000.0
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this benchmark with
 # --calib-copy 512, each scaled by the ratio of a 512 MiB device copy's known
 # bytes to what the same counter read for it.  Valid only for the encode
-# source they were taken on (sha256 below); otherwise reported as null.
+# sources they were taken on (sha256 over tq_encode.hip and tq_encode_body.inc,
+# below); otherwise reported as null.
 ENCODE_TRAFFIC = {"source_sha256": "c64c7410a72a51725ea1673f5416b2fde55896f452fa4f458b10631baa464d9a",
                   "workload": "llama3-8b-layer-b1-s32768",
                   "fetch_bytes": 68486952, "write_bytes": 14684168}
@@ -402,15 +403,22 @@ def append_steps(wl, kcb, vcb, up, steps, dev):
 def encode_traffic(workload_name):
     """Counter-measured HBM bytes of one key-encode launch, or None when the
     figures are missing or the encode source changed since they were taken."""
-    import hashlib
-    src = os.path.join(ROOT, "online_vector_quantization_amd", "csrc", "tq_encode.hip")
     t = ENCODE_TRAFFIC
     if t["source_sha256"] is None or workload_name != t["workload"]:
         return None
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != t["source_sha256"]:
-            return None
+    if encode_source_sha256() != t["source_sha256"]:
+        return None
     return t["fetch_bytes"] + t["write_bytes"]
+
+
+def encode_source_sha256():
+    """sha256 over the encode kernel's sources (tq_encode.hip, then tq_encode_body.inc)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("tq_encode.hip", "tq_encode_body.inc"):
+        with open(os.path.join(ROOT, "online_vector_quantization_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def cpu_baseline(wl, min_seconds, qjl=True):
