@@ -38,9 +38,9 @@ HBM_PEAK_GBPS = 8000.0
 # bytes to what the same counter read for it.  Valid only for the encode
 # sources they were taken on (sha256 over tq_encode.hip and tq_encode_body.inc,
 # below); otherwise reported as null.
-ENCODE_TRAFFIC = {"source_sha256": "c64c7410a72a51725ea1673f5416b2fde55896f452fa4f458b10631baa464d9a",
+ENCODE_TRAFFIC = {"source_sha256": "ab6908a12a34f63385d9038c7457a34a2bb3531b8dc35ef020e74463b52c21e2",
                   "workload": "llama3-8b-layer-b1-s32768",
-                  "fetch_bytes": 68486952, "write_bytes": 14684168}
+                  "fetch_bytes": 68483274, "write_bytes": 14684670}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attn HBM GB/s (% of peak) on compressed KV; encode Mvectors/s"
 
