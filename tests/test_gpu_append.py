@@ -1,5 +1,6 @@
 """tq_append_decode: one decode-loop step (append the new K and V, attend over
-the grown cache, advance seq_len on the device) in a single call.
+the grown cache, advance seq_len on the device) in a single call.  bf16 new
+rows take the combined key + value encode launch; fp32 rows two launches.
 
 * Equal, bit for bit, to the separate path (tq_encode_kv of the new rows into
   rows seq_len[b], then tq_decode_attention with seq_len + 1), step after step,
@@ -65,15 +66,18 @@ def _setup(B, Hkv, g, t_cap, lens, kbits, vbits, m, seed):
     return rng, kcb, vcb, kc, vc
 
 
-def _step_inputs(rng, B, Hkv, Hq):
-    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, 1, lognormal_sigma=0.5)[:, :, 0])
-    v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, 1, lognormal_sigma=0.5)[:, :, 0])
+def _step_inputs(rng, B, Hkv, Hq, kv_dtype="bf16"):
+    k = synth.kv_block(rng, B, Hkv, 1, lognormal_sigma=0.5)[:, :, 0]
+    v = synth.kv_block(rng, B, Hkv, 1, lognormal_sigma=0.5)[:, :, 0]
     q = synth.bf16_bits(rng.standard_normal((B, Hq, 128)).astype(np.float32))
-    return H.to_device(k, "bf16"), H.to_device(v, "bf16"), H.to_device(q, "bf16")
+    if kv_dtype == "bf16":
+        return H.to_device(synth.bf16_bits(k), "bf16"), H.to_device(synth.bf16_bits(v), "bf16"), H.to_device(q, "bf16")
+    return H.to_device(k, "f32"), H.to_device(v, "f32"), H.to_device(q, "bf16")
 
 
-@pytest.mark.parametrize("kbits,vbits,m,g", [(2, 3, 128, 4), (1, 2, 128, 8), (3, 3, 0, 2)])
-def test_append_decode_equals_separate_path(kbits, vbits, m, g):
+@pytest.mark.parametrize("kbits,vbits,m,g,kv_dtype", [(2, 3, 128, 4, "bf16"), (1, 2, 128, 8, "bf16"),
+                                                      (3, 3, 0, 2, "bf16"), (4, 1, 128, 1, "f32")])
+def test_append_decode_equals_separate_path(kbits, vbits, m, g, kv_dtype):
     B, Hkv, t_cap = 4, 2, 300
     lens = [250, 0, 297, 300]            # mixed, empty, filling up, already full
     Hq = Hkv * g
@@ -83,9 +87,9 @@ def test_append_decode_equals_separate_path(kbits, vbits, m, g):
     seq_b = list(lens)
     ws_a = T.alloc_workspace(B, Hq, Hkv, t_cap, H.DEV)
     steps = 5
-    _log(f"append_decode kbits={kbits} vbits={vbits} m={m} g={g} lens={lens} steps={steps}")
+    _log(f"append_decode kbits={kbits} vbits={vbits} m={m} g={g} kv={kv_dtype} lens={lens} steps={steps}")
     for s in range(steps):
-        kn, vn, q = _step_inputs(rng, B, Hkv, Hq)
+        kn, vn, q = _step_inputs(rng, B, Hkv, Hq, kv_dtype)
         out_a = T.append_decode(kcb, vcb, kn, vn, q, kc_a, vc_a, seq_a, workspace=ws_a)
         # separate path
         app = [b for b in range(B) if 0 <= seq_b[b] < t_cap]
