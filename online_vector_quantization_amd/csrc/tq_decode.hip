@@ -216,14 +216,10 @@ __device__ __forceinline__ void lds_store_g(float *p, const float (&v)[G]) {
 
 // Query-specific lookup tables (sign table, and the key tables below) hold,
 // per nibble position p and nibble value n, one float per head.  Layout: for
-// g <= 4 entry (p, n) is g consecutive floats; for g = 8 the heads are split
-// into two quads, [p][quad][n][4], so that the 64 lanes reading one position
+// g <= 4 entry (p, n) is g consecutive floats, float offset (16 p + n) g + h;
+// for g = 8 the heads are split into two quads, [p][quad][n][4], offset
+// ((2 p + h / 4) 16 + n) 4 + h % 4, so that the 64 lanes reading one position
 // (each its own n) touch every LDS bank at most once per 16-byte read.
-template <int G>
-__device__ __forceinline__ int tab_offset(int p, int n, int h) {
-  if constexpr (G <= 4) return (p * 16 + n) * G + h;
-  return ((p * (G / 4) + h / 4) * 16 + n) * 4 + (h & 3);
-}
 
 // Ordering without instructions: x is made to depend on the g values d, so
 // whatever uses x waits for them.  One asm statement per call: the compiler
@@ -296,7 +292,7 @@ __device__ __forceinline__ void tab_load_off(const float *tab, int p, uint32_t o
   }
 }
 
-// Entry index e of a table with P positions -> (p, n, h), the inverse of tab_offset.
+// Float offset e of a table entry -> (p, n, h), the inverse of the layout above.
 template <int G>
 __device__ __forceinline__ void tab_entry(int e, int &p, int &n, int &h) {
   p = e / (16 * G);
