@@ -15,7 +15,9 @@ position seq_len - n_new + j attending causally over the compressed cache.
   (5e-4 at the full 8B layer, whose outlier channels make large logits).
 * Full size: 8 queries per head (32 rows per kv head: the matrix-core path)
   over the Llama-3-8B-shaped layer (32768 tokens): every query against the
-  single-query decode, two against the oracle.
+  single-query decode, two against the oracle; and the batched workload's
+  shape (16 x 8 x 8192, ragged lengths, 4 queries per head): every query
+  against the single-query decode, two sequences against the oracle.
 """
 import sys
 
@@ -135,4 +137,37 @@ def test_chunk_llama8b_full():
                                  H.oracle_book(3, 0))
         err = np.abs(g_np[:, :, j] - ref).max()
         _log(f"  query {j}: max-abs error {err:.2e}")
+        assert err <= 2e-3
+
+
+def test_chunk_batched_full():
+    """The batched workload's shape (16 sequences x 8 kv heads x 8192 tokens,
+    32 q heads) with 4 new queries per head: 16 rows per kv head, the
+    matrix-core path, ragged lengths."""
+    wl = synth.batched(2)
+    B, Hkv, S = wl.batch, wl.n_kv_heads, wl.seq_len
+    n_new = 4
+    _log(f"{wl.name}: {n_new} causal queries per head, ragged lengths")
+    kcb, vcb = H.gpu_book(1, 128), H.gpu_book(2, 0)
+    kc, vc = H.build_cache(kcb, vcb, H.to_device(wl.k, "bf16"), H.to_device(wl.v, "bf16"), B, Hkv, S, S)
+    rng = np.random.default_rng(12)
+    q = H.to_device(synth.bf16_bits(rng.standard_normal((B, 32, n_new, 128)).astype(np.float32)), "bf16")
+    lens = [S - 301 * b for b in range(B)]
+    sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+    got = T.chunk_attention(kcb, vcb, q, kc, vc, sl)
+    per = _per_query_decode(kcb, vcb, q, kc, vc, lens)
+    torch.cuda.synchronize()
+    g_np = got.cpu().numpy()
+    diff = np.abs(g_np - per.cpu().numpy()).max()
+    _log(f"  vs single-query decode: max-abs {diff:.2e}")
+    assert diff <= 2e-3
+    # two sequences against the oracle
+    kh, vh = H.cache_to_host(kc), H.cache_to_host(vc)
+    q_host = q.float().cpu().numpy().astype(np.float64)
+    for b in (0, B - 1):
+        sub = lambda c: {k: (None if v is None else v[b:b + 1]) for k, v in c.items()}
+        ref = O.chunk_attention(q_host[b:b + 1], sub(kh), sub(vh), [lens[b]], H.oracle_book(1, 128),
+                                H.oracle_book(2, 0))
+        err = np.abs(g_np[b:b + 1] - ref).max()
+        _log(f"  sequence {b}: max-abs error vs oracle {err:.2e}")
         assert err <= 2e-3
