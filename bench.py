@@ -230,6 +230,12 @@ def main():
             "avg_us_qprep_partial_combine": round(dec_ms * 1e3, 2),
         },
         "wall_s_timed": round(wall, 4),
+        "launch_us_percentiles": {
+            name: {"p10": round(float(np.percentile(arr, 10)) * 1e3, 2),
+                   "median": round(float(np.median(arr)) * 1e3, 2),
+                   "p90": round(float(np.percentile(arr, 90)) * 1e3, 2)}
+            for name, arr in (("encode_keys", enc_k), ("encode_values", enc_v), ("decode", dec))},
+        "copy_gbps_context": copy_bandwidth(dev),
     }
     line["attention_logits"] = logits_only(T, kcb, q, caches, seq, ws, n_vec * k_rec, B * Hq * S * 4, args, dev)
     if args.chunk > 0:
@@ -239,6 +245,26 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, qjl=bool(qjl_m))
     print(json.dumps(line), flush=True)
+
+
+def copy_bandwidth(dev, mib=1024, reps=5):
+    """A plain 1 GiB device-to-device copy (torch), timed with events: read +
+    write bytes per second.  Context for the HBM fractions, not a peak."""
+    import torch
+    n = mib << 18
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    gbps = 2 * n * 4 * reps / (start.elapsed_time(end) * 1e-3) / 1e9
+    del src, dst
+    return round(gbps, 1)
 
 
 def logits_only(T, kcb, q, caches, seq, ws, key_bytes, logit_bytes, args, dev):
