@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama8b", choices=["llama8b", "llama70b", "batched2", "batched4"])
+    ap.add_argument("--config", default="llama8b", choices=["llama8b", "llama70b", "batched2", "batched4", "bulk"],
+                    help="bulk: encode 16,777,216 K and V vectors, then 64 queries over a 262144 x 8 view")
     ap.add_argument("--hot", action="store_true", help="no replica rotation (cache-resident numbers)")
     ap.add_argument("--append-steps", type=int, default=0, metavar="N",
                     help="also time N decode-loop steps (append one token per sequence and head, then attend): "
@@ -92,6 +93,9 @@ def main():
         sys.exit(1)
     T.load_library()
     dev = torch.device("cuda", 0)
+    if args.config == "bulk":
+        print(json.dumps(bench_bulk(args, T, dev)), flush=True)
+        return
     t0 = time.time()
     wl = workload(args.config)
     B, Hq, Hkv, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.seq_len
@@ -245,6 +249,142 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, qjl=bool(qjl_m))
     print(json.dumps(line), flush=True)
+
+
+def bench_bulk(args, T, dev):
+    """Prefill-scale bulk encode: every step encodes 16,777,216 K vectors (b' = 3
+    + QJL) and 16,777,216 V vectors (4-bit), then decodes 64 q heads (8 per kv
+    head) over the first 2,097,152 rows of each cache viewed as [1, 8, 262144].
+    The inputs (8.6 GB) and the decode view (294 MB) exceed the 256 MB
+    Infinity Cache, so every launch reads HBM."""
+    import torch
+    from online_vector_quantization_amd import synth
+    n, Tlen, Hkv, Hq = 16_777_216, 262_144, 8, 64
+    t0 = time.time()
+    kx, vx, q = synth.bulk_device(n, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] bulk inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    kcb = T.Codebook(128, 3, 128, 0, 1, device=0)
+    vcb = T.Codebook(128, 4, 0, 0, 1, device=0)
+    kc = T.CompressedCache.allocate(kcb, 1, 1, n)
+    vc = T.CompressedCache.allocate(vcb, 1, 1, n)
+    rows = Hkv * Tlen
+    kview = T.CompressedCache(kc.codes.reshape(-1, kcb.code_words)[:rows].reshape(1, Hkv, Tlen, -1),
+                              kc.norms.reshape(-1)[:rows].reshape(1, Hkv, Tlen),
+                              kc.signs.reshape(-1, kcb.sign_words)[:rows].reshape(1, Hkv, Tlen, -1),
+                              kc.res_norms.reshape(-1)[:rows].reshape(1, Hkv, Tlen))
+    vview = T.CompressedCache(vc.codes.reshape(-1, vcb.code_words)[:rows].reshape(1, Hkv, Tlen, -1),
+                              vc.norms.reshape(-1)[:rows].reshape(1, Hkv, Tlen))
+    seq = torch.full((1,), Tlen, dtype=torch.int32, device=dev)
+    ws = T.alloc_workspace(1, Hq, Hkv, Tlen, dev)
+    out = torch.empty(1, Hq, 128, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(marks=None):
+        if marks:
+            marks[0].record(stream)
+        T.encode_into_cache(kcb, kx, kc, stream=stream)
+        if marks:
+            marks[1].record(stream)
+        T.encode_into_cache(vcb, vx, vc, stream=stream)
+        if marks:
+            marks[2].record(stream)
+        T.decode_attention(kcb, vcb, q, kview, vview, seq, out=out, workspace=ws, stream=stream)
+        if marks:
+            marks[3].record(stream)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    steps = max(1, args.steps)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [(ev(), ev(), ev(), ev()) for _ in range(steps)]
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s_ in range(steps):
+        step(marks[s_])
+    end.record(stream)
+    torch.cuda.synchronize()
+    enc_k = np.array([m[0].elapsed_time(m[1]) for m in marks])
+    enc_v = np.array([m[1].elapsed_time(m[2]) for m in marks])
+    dec = np.array([m[2].elapsed_time(m[3]) for m in marks])
+    k_rec = 4 * kcb.code_words + 4 * kcb.sign_words + 8
+    v_rec = 4 * vcb.code_words + 4
+    dec_bytes = rows * (k_rec + v_rec)
+    dec_gbps = dec_bytes / (dec.mean() * 1e-3) / 1e9
+    enc_k_bytes, enc_v_bytes = n * (256 + k_rec), n * (256 + v_rec)
+    enc_k_gbps = enc_k_bytes / (enc_k.mean() * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(dec_gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(start.elapsed_time(end) / steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "bulk-encode-16777216-kv-then-decode-g8-s262144", "vectors": n, "key_bits": 4,
+                   "value_bits": 4, "qjl_dim": 128, "decode_view": [1, Hkv, Tlen], "q_heads": Hq,
+                   "input_dtype": "bf16", "key_mode": "(b-1)-bit codes + 1-bit QJL",
+                   "step": "encode all K and V vectors, then one decode step over the view"},
+        "decode_frac_of_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "decode_us": round(float(dec.mean()) * 1e3, 2),
+        "encode_mvectors_per_s": round(2 * n / ((enc_k.mean() + enc_v.mean()) * 1e-3) / 1e6, 1),
+        "encode_us": {"keys": round(float(enc_k.mean()) * 1e3, 1), "values": round(float(enc_v.mean()) * 1e3, 1)},
+        "roofline": {"kernel": "encode (keys: rotation + QJL)", "bound": "hbm", "achieved": round(enc_k_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": enc_k_bytes,
+                     "avg_launch_us": round(float(enc_k.mean()) * 1e3, 1)},
+        "roofline_values_encode": {"bound": "hbm", "achieved": round(enc_v_bytes / (enc_v.mean() * 1e-3) / 1e9, 1),
+                                   "peak": HBM_PEAK_GBPS, "unit": "GB/s", "algorithmic_bytes_per_launch": enc_v_bytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bulk(kx, vx, q, args.cpu_seconds)
+    return line
+
+
+def cpu_baseline_bulk(kx, vx, q, min_seconds):
+    """The oracle on a bounded sample of the bulk step: encode of the first
+    2^17 K and V vectors, decode of the 64 q heads over the 8-head cache of
+    16384 tokens built from them; reported as encode vectors/s and decode GB/s
+    of compressed bytes read."""
+    import torch
+    import oracle as O
+    from online_vector_quantization_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    ns, Hkv = 1 << 17, 8
+    Tlen = ns // Hkv
+
+    def host_f32(t):
+        return synth.bf16_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+    k, v = host_f32(kx[:ns]), host_f32(vx[:ns])
+    qh = host_f32(q).astype(np.float64)
+    c_k, t_k = O.build_codebook(128, 3)
+    c_v, t_v = O.build_codebook(128, 4)
+    Pi, Sm = O.haar_rotation(128, 0), O.qjl_matrix(128, 128, 1)
+    shape = (1, Hkv, ns // Hkv)
+    t_enc = t_dec = 0.0
+    reps = 0
+    while reps == 0 or t_enc + t_dec < min_seconds:
+        t0 = time.perf_counter()
+        ek = O.encode(k, Pi, c_k, t_k, Sm)
+        ev = O.encode(v, Pi, c_v, t_v)
+        kcache = {"codes": O.pack_bits(ek["idx"], 3).reshape(*shape, -1), "signs": O.pack_bits(ek["z"], 1).reshape(*shape, -1),
+                  "norms": ek["nu"].reshape(shape), "res_norms": ek["gamma"].reshape(shape)}
+        vcache = {"codes": O.pack_bits(ev["idx"], 4).reshape(*shape, -1), "norms": ev["nu"].reshape(shape)}
+        t1 = time.perf_counter()
+        O.decode_attention(qh, kcache, vcache, [Tlen], {"bits": 3, "centroids": c_k, "Pi": Pi, "S": Sm},
+                           {"bits": 4, "centroids": c_v, "Pi": Pi})
+        t2 = time.perf_counter()
+        t_enc += t1 - t0
+        t_dec += t2 - t1
+        reps += 1
+    rec = (4 * 12 + 16 + 8) + (4 * 16 + 4)
+    return {"value": round(reps * Hkv * Tlen * rec / t_dec / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle", "encode_mvectors_per_s": round(reps * 2 * ns / t_enc / 1e6, 4),
+            "sample": f"{reps}x: oracle encode of the first {ns} K and {ns} V vectors ({t_enc / reps:.2f}s each), "
+                      f"then oracle decode of 64 q heads over {Tlen} tokens x {Hkv} kv heads built from them "
+                      f"({t_dec / reps:.2f}s each)"}
 
 
 def copy_bandwidth(dev, mib=1024, reps=5):
