@@ -38,9 +38,9 @@ HBM_PEAK_GBPS = 8000.0
 # bytes to what the same counter read for it.  Valid only for the encode
 # sources they were taken on (sha256 over tq_encode.hip and tq_encode_body.inc,
 # below); otherwise reported as null.
-ENCODE_TRAFFIC = {"source_sha256": "ab6908a12a34f63385d9038c7457a34a2bb3531b8dc35ef020e74463b52c21e2",
+ENCODE_TRAFFIC = {"source_sha256": "d6229989d1b4806eb7617f864ab0e949205112be30e940cbffb24cf6b395f4f0",
                   "workload": "llama3-8b-layer-b1-s32768",
-                  "fetch_bytes": 68483274, "write_bytes": 14684670}
+                  "fetch_bytes": 68507571, "write_bytes": 14710275}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode-attn HBM GB/s (% of peak) on compressed KV; encode Mvectors/s"
 

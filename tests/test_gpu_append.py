@@ -152,3 +152,38 @@ def test_append_decode_graph_replay():
         assert seq_g.cpu().tolist() == [8193 + s] * B
     _same_cache(kc_g, kc_e)
     _same_cache(vc_g, vc_e)
+
+
+def test_append_decode_wide_batch():
+    # 460 sequences x 8 kv heads (3,680 rows, one token chunk each) with
+    # ragged, empty and full sequences.  Same bar: bit for bit the separate
+    # path, step after step, and the oracle at the end.
+    B, Hkv, g, t_cap = 460, 8, 1, 24
+    rng0 = np.random.default_rng(77)
+    lens = [int(x) for x in rng0.integers(0, t_cap + 1, size=B)]
+    lens[0], lens[1], lens[2] = 0, t_cap, t_cap - 1
+    Hq = Hkv * g
+    rng, kcb, vcb, kc_a, vc_a = _setup(B, Hkv, g, t_cap, lens, 2, 3, 128, seed=78)
+    kc_b, vc_b = _clone(kc_a), _clone(vc_a)
+    seq_a = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+    seq_b = list(lens)
+    ws_a = T.alloc_workspace(B, Hq, Hkv, t_cap, H.DEV)
+    _log(f"append_decode wide: B={B} Hkv={Hkv} g={g} t_cap={t_cap}")
+    for s in range(3):
+        kn, vn, q = _step_inputs(rng, B, Hkv, Hq)
+        out_a = T.append_decode(kcb, vcb, kn, vn, q, kc_a, vc_a, seq_a, workspace=ws_a)
+        app = [b for b in range(B) if 0 <= seq_b[b] < t_cap]
+        rows = torch.tensor([(b * Hkv + h) * t_cap + seq_b[b] for b in app for h in range(Hkv)],
+                            dtype=torch.int64, device=H.DEV)
+        sel = torch.tensor([b * Hkv + h for b in app for h in range(Hkv)], dtype=torch.int64, device=H.DEV)
+        T.encode_into_cache(kcb, kn.reshape(-1, 128)[sel].contiguous(), kc_b, dst_row=rows)
+        T.encode_into_cache(vcb, vn.reshape(-1, 128)[sel].contiguous(), vc_b, dst_row=rows)
+        attend = [min(s_ + 1, t_cap) for s_ in seq_b]
+        out_b = T.decode_attention(kcb, vcb, q, kc_b, vc_b, torch.tensor(attend, dtype=torch.int32, device=H.DEV))
+        seq_b = [s_ + 1 if 0 <= s_ < t_cap else s_ for s_ in seq_b]
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out_a.cpu().numpy().view(np.uint32), out_b.cpu().numpy().view(np.uint32))
+        assert seq_a.cpu().tolist() == seq_b
+    _same_cache(kc_a, kc_b)
+    _same_cache(vc_a, vc_b)
+    H.check_decode(kcb, vcb, q, kc_a, vc_a, seq_b, 2, 3, 128)

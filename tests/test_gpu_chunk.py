@@ -171,3 +171,30 @@ def test_chunk_batched_full():
         err = np.abs(g_np[b:b + 1] - ref).max()
         _log(f"  sequence {b}: max-abs error vs oracle {err:.2e}")
         assert err <= 2e-3
+
+
+def test_chunk_decode_kernel_wide_batch():
+    # 40 sequences x 16 kv heads x 7 queries (g = 1: the decode kernel, 4,480
+    # query rows in the grid's y and z) over ragged windows.  Oracle parity at
+    # the 2e-3 bar.
+    B, Hkv, g, n_new, t_cap = 40, 16, 1, 7, 80
+    rng = np.random.default_rng(91)
+    lens = [int(x) for x in rng.integers(n_new, t_cap + 1, size=B)]
+    lens[0] = 3   # its first queries see nothing
+    Hq = Hkv * g
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap, lognormal_sigma=0.5))
+    v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap, lognormal_sigma=0.5))
+    q = H.to_device(synth.bf16_bits(rng.standard_normal((B, Hq, n_new, 128)).astype(np.float32)), "bf16")
+    kcb, vcb = H.gpu_book(2, 128), H.gpu_book(3, 0)
+    kc, vc = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, t_cap, t_cap)
+    sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+    _log(f"chunk two-launch merge: B={B} Hkv={Hkv} n_new={n_new} t_cap={t_cap}")
+    got = T.chunk_attention(kcb, vcb, q, kc, vc, sl)
+    torch.cuda.synchronize()
+    g_np = got.cpu().numpy()
+    ref = O.chunk_attention(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), H.cache_to_host(vc),
+                            lens, H.oracle_book(2, 128), H.oracle_book(3, 0))
+    err = np.abs(g_np - ref).max()
+    _log(f"  vs oracle: max-abs {err:.2e}")
+    assert err <= 2e-3, f"max-abs error {err:.3e}"
+    assert np.all(g_np[0, :, :n_new - 3] == 0.0)
