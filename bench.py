@@ -231,7 +231,8 @@ def main():
         "roofline_decode": {
             "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": dec_bytes,
-            "avg_us_qprep_partial_combine": round(dec_ms * 1e3, 2),
+            "avg_us_partial_and_combine": round(dec_ms * 1e3, 2),
+            "alu": decode_alu_view(B * Hq * S, qjl_m, dec_ms),
         },
         "wall_s_timed": round(wall, 4),
         "launch_us_percentiles": {
@@ -332,10 +333,28 @@ def bench_bulk(args, T, dev):
                      "avg_launch_us": round(float(enc_k.mean()) * 1e3, 1)},
         "roofline_values_encode": {"bound": "hbm", "achieved": round(enc_v_bytes / (enc_v.mean() * 1e-3) / 1e9, 1),
                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "algorithmic_bytes_per_launch": enc_v_bytes},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": dec_bytes,
+                            "alu": decode_alu_view(Hq * Tlen, 128, float(dec.mean()))},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_bulk(kx, vx, q, args.cpu_seconds)
     return line
+
+
+# Non-packed fp32 vector FMA issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# (78.6 TFLOP/s counting an FMA as two flops; packed fp32 is not built).
+ALU_PEAK_T_FMA = 39.3216
+
+
+def decode_alu_view(token_heads, qjl_m, ms):
+    """The decode against the vector-ALU roof: per (token, q head) the method
+    needs d multiply-adds for the codebook dot product, m for the sign term and
+    d for the value sum (384 at d = m = 128), as fp32 lane FMAs per second."""
+    fma = token_heads * (128 + qjl_m + 128)
+    achieved = fma / (ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": round(achieved, 2), "peak": ALU_PEAK_T_FMA, "unit": "T FMA/s (fp32 lanes)",
+            "frac": round(achieved / ALU_PEAK_T_FMA, 4), "algorithmic_fma_per_launch": fma}
 
 
 def cpu_baseline_bulk(kx, vx, q, min_seconds):
