@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama8b", choices=["llama8b", "llama70b", "batched2", "batched4", "bulk"],
+    ap.add_argument("--config", default="llama8b", choices=["llama8b", "llama70b", "batched2", "batched4", "bulk", "tiny"],
                     help="bulk: encode 16,777,216 K and V vectors, then 64 queries over a 262144 x 8 view")
     ap.add_argument("--hot", action="store_true", help="no replica rotation (cache-resident numbers)")
     ap.add_argument("--append-steps", type=int, default=0, metavar="N",
@@ -95,6 +95,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.config == "bulk":
         print(json.dumps(bench_bulk(args, T, dev)), flush=True)
+        return
+    if args.config == "tiny":
+        print(json.dumps(bench_tiny(args, T, dev)), flush=True)
         return
     t0 = time.time()
     wl = workload(args.config)
@@ -340,6 +343,64 @@ def bench_bulk(args, T, dev):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_bulk(kx, vx, q, args.cpu_seconds)
     return line
+
+
+def bench_tiny(args, T, dev):
+    """The tiny workload: 4096 fp32 keys (2-bit codes + 128 QJL signs), one query.
+    It is latency-bound, so the line reports launch times next to the quality of
+    the score estimate: exact q.k against the estimate (bias, RMSE, correlation)
+    and softmax at scale 1/sqrt(d) of both (max-abs difference, total
+    variation).  The values reuse the keys at 2 bits (the workload has none)."""
+    import torch
+    from online_vector_quantization_amd import synth
+    wl = synth.tiny()
+    n = 4096
+    kcb = T.Codebook(128, 2, 128, 0, 1, device=0)
+    vcb = T.Codebook(128, 2, 0, 0, 1, device=0)
+    k = torch.from_numpy(wl.k.reshape(n, 128).copy()).to(dev)
+    q = torch.from_numpy(wl.q.copy()).to(dev)
+    kc, vc = T.CompressedCache.allocate(kcb, 1, 1, n), T.CompressedCache.allocate(vcb, 1, 1, n)
+    seq = torch.tensor([n], dtype=torch.int32, device=dev)
+    ws = T.alloc_workspace(1, 1, 1, n, dev)
+    out = torch.empty(1, 1, 128, dtype=torch.float32, device=dev)
+    scores = torch.zeros(1, 1, n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    steps = max(args.steps, 1)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.warmup + steps)]
+    for i, e in enumerate(ev):
+        e[0].record(stream)
+        T.encode_into_cache(kcb, k, kc, stream=stream)
+        T.encode_into_cache(vcb, k, vc, stream=stream)
+        e[1].record(stream)
+        T.decode_attention(kcb, vcb, q, kc, vc, seq, out=out, workspace=ws, stream=stream,
+                           dbg_scores=scores if i == 0 else None)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    enc = np.array([e[0].elapsed_time(e[1]) for e in ev[args.warmup:]])
+    dec = np.array([e[1].elapsed_time(e[2]) for e in ev[args.warmup:]])
+    exact = wl.k.reshape(n, 128).astype(np.float64) @ wl.q.reshape(128).astype(np.float64)
+    est = scores.cpu().numpy()[0, 0].astype(np.float64) * math.sqrt(128.0)
+    err = est - exact
+
+    def softmax(x):
+        e_ = np.exp(x - x.max())
+        return e_ / e_.sum()
+    p, ph = softmax(exact / math.sqrt(128.0)), softmax(est / math.sqrt(128.0))
+    dec_bytes = n * T.compressed_bytes_per_token(kcb, vcb)
+    dec_gbps = dec_bytes / (float(dec.mean()) * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(dec_gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(float((enc + dec).mean()), 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "keys": n, "head_dim": 128, "key_bits": 3, "qjl_dim": 128,
+                   "input_dtype": "f32", "step": "encode the keys (and the same vectors as 2-bit values), then decode"},
+        "encode_us": round(float(enc.mean()) * 1e3, 2), "decode_us": round(float(dec.mean()) * 1e3, 2),
+        "quality": {"bias": round(float(err.mean()), 5), "bias_se": round(float(err.std() / math.sqrt(n)), 5),
+                    "rmse": round(float(math.sqrt(np.mean(err * err))), 5),
+                    "corr": round(float(np.corrcoef(est, exact)[0, 1]), 5),
+                    "softmax_max_abs": round(float(np.abs(p - ph).max()), 6),
+                    "softmax_tv": round(float(0.5 * np.abs(p - ph).sum()), 5)},
+    }
 
 
 # Non-packed fp32 vector FMA issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz

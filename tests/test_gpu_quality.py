@@ -80,3 +80,28 @@ def test_inner_product_bias_mse_only_vs_qjl(b):
     assert 1.0 - s_mse > 5.0 * se_mse
     # (b-1) + 1 QJL: unbiased
     assert abs(s_qjl - 1.0) < 4.0 * se_qjl + 1e-3
+
+
+def test_tiny_config_report_matches_oracle():
+    # The tiny workload through the library (fp32 keys, b = 3: 2-bit codes + QJL; the values
+    # reuse the keys at 2 bits): its quality report equals the oracle's, whose unbiasedness and
+    # closed-form RMSE tests/test_tiny_report.py pins.
+    from test_tiny_report import oracle_tiny, tiny_report
+    wl = synth.tiny()
+    kcb, vcb = H.gpu_book(2, 128), H.gpu_book(2, 0)
+    k = H.to_device(wl.k.reshape(-1, 128), "f32")
+    kc, vc = H.build_cache(kcb, vcb, k.reshape(1, 1, 4096, 128), k.reshape(1, 1, 4096, 128), 1, 1, 4096, 4096)
+    scores = torch.zeros(1, 1, 4096, dtype=torch.float32, device=H.DEV)
+    T.decode_attention(kcb, vcb, H.to_device(wl.q, "f32"), kc, vc,
+                       torch.tensor([4096], dtype=torch.int32, device=H.DEV), dbg_scores=scores)
+    torch.cuda.synchronize()
+    est = scores.cpu().numpy()[0, 0].astype(np.float64) * math.sqrt(128.0)
+    exact, est_o, _, _, _, _, _ = oracle_tiny()
+    got, ref = tiny_report(est, exact), tiny_report(est_o, exact)
+    print("tiny report (GPU):   ", {k_: round(v, 5) for k_, v in got.items()}, file=sys.stderr, flush=True)
+    print("tiny report (oracle):", {k_: round(v, 5) for k_, v in ref.items()}, file=sys.stderr, flush=True)
+    assert abs(got["bias"]) <= 3 * got["bias_se"]
+    assert abs(got["rmse"] / ref["rmse"] - 1) < 1e-3
+    assert abs(got["corr"] - ref["corr"]) < 1e-4
+    assert abs(got["softmax_tv"] - ref["softmax_tv"]) < 1e-3
+    assert abs(got["softmax_max_abs"] - ref["softmax_max_abs"]) < 1e-4
