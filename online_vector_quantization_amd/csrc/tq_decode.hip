@@ -32,10 +32,11 @@
 //       (records read as one coalesced block); lane (token group, coordinate
 //       group) accumulates 8 rotated coordinates x g heads over 16 tokens,
 //       a pair table dequantizing two codes per lookup.
-//  2. the waves merge; the chunk's (max, sum, rotated output) go to the
+//  2. the waves merge; the chunk's (max, sum) and its partial output, rotated
+//     back by Pi_v^T (linear, so it commutes with the merge), go to the
 //     workspace.
-// A second, small launch merges the chunks of each (b, q head) (log-sum-exp),
-// applies Pi_v^T and writes the output.
+// A second, small launch merges the chunks of each (b, q head) (log-sum-exp)
+// and writes the output.
 //
 // The same kernel serves two more calls: with SC (scores only) it ends after
 // the key phase of each tile and writes every l_t (no values, no merge, no
@@ -173,10 +174,14 @@ template <int G> struct Lds {
     uint32_t vrec[GM::kWaves][64 * 16 + 4];   // a tile's value code words, records back to back (+ pad)
     float wts[GM::kWaves][64 * G];            // per token, the g heads' weights p * nu_v
   };
+  struct Epi {      // after the loop
+    float merge[GM::kWaves][G][D];   // per-wave rotated sums; then the 4 partial products of Pi_v^T
+    float ot[G][D];                  // the work-group's rotated sum
+  };
   union Shared {
     Pro pro;
     Loop loop;
-    float merge[GM::kWaves][G][D];
+    Epi epi;
   };
 };
 
@@ -711,6 +716,15 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   if constexpr (SC) return;   // uniform: no barrier follows for any thread
 
   // ------------------------------------------------------------ 2. merge waves
+  // The chunk's partial output leaves the work-group rotated back, o = Pi_v^T o~
+  // (linear, so the merge of the chunks commutes with it): thread (i4, q4)
+  // applies rows 32 q4 .. 32 q4 + 31 of column i4 of Pi_v, requested now so
+  // that the wave merge hides their latency.
+  static_assert(kThreads == 4 * D, "the inverse rotation maps 512 threads to (coordinate, quarter)");
+  const int i4 = tid & (D - 1), q4 = tid >> 7;
+  float pvr[32];
+#pragma unroll
+  for (int jj = 0; jj < 32; ++jj) pvr[jj] = a.rot_v[(32 * q4 + jj) * D + i4];
   float l_wave[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -737,17 +751,37 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
     const float f = (m_run[h] == -INFINITY) ? 0.f : __expf(m_run[h] - mx);
     if (tg == 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sh.merge[wave][h][8 * cg + k] = acc[h][k] * f;
+      for (int k = 0; k < 8; ++k) sh.epi.merge[wave][h][8 * cg + k] = acc[h][k] * f;
     }
   }
   __syncthreads();
-  float *part_o = a.ws_part_o + static_cast<int64_t>(group_id) * G * D;
   for (int e = tid; e < G * D; e += kThreads) {
     const int h = e / D, j = e % D;
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += sh.merge[w][h][j];
-    part_o[e] = s;
+    for (int w = 0; w < kWaves; ++w) s += sh.epi.merge[w][h][j];
+    sh.epi.ot[h][j] = s;
+  }
+  __syncthreads();
+  {
+    float r[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) r[h] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj)
+#pragma unroll
+      for (int h = 0; h < G; ++h) r[h] = fmaf(pvr[jj], sh.epi.ot[h][32 * q4 + jj], r[h]);
+    // the quarters' products go where the per-wave sums were (read before the barrier above)
+    float *red = &sh.epi.merge[0][0][0];   // [4][G][D]
+#pragma unroll
+    for (int h = 0; h < G; ++h) red[(q4 * G + h) * D + i4] = r[h];
+  }
+  __syncthreads();
+  float *part_o = a.ws_part_o + static_cast<int64_t>(group_id) * G * D;
+  {
+    const float *red = &sh.epi.merge[0][0][0];
+    for (int e = tid; e < G * D; e += kThreads)
+      part_o[e] = red[e] + red[G * D + e] + red[2 * G * D + e] + red[3 * G * D + e];
   }
   if (tid < G) {
     const int h = tid;
@@ -763,10 +797,11 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   }
 }
 
-// Merge of the chunks of one (b, q head): log-sum-exp weights, rotated sum,
-// then o = Pi_v^T o~.  A separate launch: the kernel boundary makes every
-// chunk's partials visible across XCDs without an in-kernel device fence.
-// Every global read (the chunks' (max, sum), their partial outputs and this
+// Merge of the chunks of one (b, q head) for the matrix-core chunk kernel,
+// whose partial outputs stay rotated: log-sum-exp weights, rotated sum, then
+// o = Pi_v^T o~.  A separate launch: the kernel boundary makes every chunk's
+// partials visible across XCDs without an in-kernel device fence.  Every
+// global read (the chunks' (max, sum), their partial outputs and this
 // thread's slice of Pi_v) is issued before the first barrier.
 constexpr int kCombThreads = 512;
 constexpr int kCombPer = kMaxDecodeChunks / 4;   // partial outputs per thread
@@ -858,6 +893,71 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
   }
 }
 
+// Merge of the chunks of one (b, q head) for the decode kernel, whose partial
+// outputs are already rotated back: o = sum_c w_c o_c / sum_c w_c l_c with
+// w_c = exp(m_c - max m).  Two waves, thread i = output coordinate i; each
+// wave forms the chunk weights itself, so no work-group barrier is needed.
+// Every global read is issued before the weights are formed.
+constexpr int kOutThreads = 128;
+constexpr int kOutRegs = 32;   // partial outputs held in registers; more chunks are read in a loop
+
+__global__ __launch_bounds__(kOutThreads) void combine_out_kernel(DecodeArgs a) {
+  __shared__ float s_w[kOutThreads / 64][kMaxDecodeChunks];
+  const int bhq = blockIdx.x;                  // (b * Hq + q head) * n_new + query
+  const int jq = bhq % a.n_new;
+  const int b = bhq / a.n_new / a.n_q_heads;
+  const int hq = bhq / a.n_new % a.n_q_heads;
+  const int g = a.n_q_heads / a.n_kv_heads;
+  const int hk = hq / g, h = hq % g;
+  const int qrow = (b * a.n_kv_heads + hk) * a.n_new + jq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nc = a.n_chunks;
+  const int64_t grp0 = static_cast<int64_t>(qrow) * nc;
+  const float *po = a.ws_part_o + (grp0 * g + h) * D + tid;   // chunk c at + c * g * D
+  const int64_t cstride = static_cast<int64_t>(g) * D;
+  float pr[kOutRegs];
+#pragma unroll
+  for (int c = 0; c < kOutRegs; ++c) pr[c] = (c < nc) ? po[c * cstride] : 0.f;
+  float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
+  if (lane < nc) {
+    m0 = a.ws_part_ml[((grp0 + lane) * g + h) * 2];
+    l0 = a.ws_part_ml[((grp0 + lane) * g + h) * 2 + 1];
+  }
+  if (lane + 64 < nc) {
+    m1 = a.ws_part_ml[((grp0 + lane + 64) * g + h) * 2];
+    l1 = a.ws_part_ml[((grp0 + lane + 64) * g + h) * 2 + 1];
+  }
+  static_assert(kMaxDecodeChunks <= 128, "two chunk weights per lane");
+  if (!(l0 > 0.f)) m0 = -INFINITY;
+  if (!(l1 > 0.f)) m1 = -INFINITY;
+  const float mx = wave_max(fmaxf(m0, m1));
+  const float w0 = (m0 == -INFINITY) ? 0.f : __expf(m0 - mx);
+  const float w1 = (m1 == -INFINITY) ? 0.f : __expf(m1 - mx);
+  const float tot = wave_sum(w0 * l0 + w1 * l1);
+  const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
+  s_w[wave][lane] = w0 * inv;
+  s_w[wave][lane + 64] = w1 * inv;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float o = 0.f;
+#pragma unroll
+  for (int c = 0; c < kOutRegs; ++c) o = fmaf(s_w[wave][c], pr[c], o);
+  for (int c = kOutRegs; c < nc; ++c) o = fmaf(s_w[wave][c], po[c * cstride], o);
+  const int64_t o_idx = static_cast<int64_t>(bhq) * D + tid;
+  if (a.out_bf16) {
+    static_cast<uint16_t *>(a.out)[o_idx] = f32_to_bf16_rne(o);
+  } else {
+    static_cast<float *>(a.out)[o_idx] = o;
+  }
+  // Append steps: the sequence has one more cached token (the main kernel,
+  // the only reader of seq_len, has completed).
+  if (a.seq_inc != nullptr && hq == 0 && jq == 0 && tid == 0) {
+    const int32_t sl = a.seq_inc[b];
+    if (sl >= 0 && sl < a.t_cap) a.seq_inc[b] = sl + 1;
+  }
+}
+
 template <int KB, bool QJL, bool SC>
 hipError_t launch_g(const DecodeArgs &a, int g, dim3 grid, hipStream_t stream) {
   switch (g) {
@@ -929,9 +1029,11 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  if (a.n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
   const hipError_t e = launch_main<false>(a, stream);
   if (e != hipSuccess) return e;
-  return launch_combine(a, stream);
+  hipLaunchKernelGGL(combine_out_kernel, dim3(a.batch * a.n_q_heads * a.n_new), dim3(kOutThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_logits(const DecodeArgs &a, hipStream_t stream) {

@@ -125,7 +125,7 @@ struct DecodeArgs {
   const float *v_lut;      // value pair table (kPairLutBytes)
   const float *k_pair;     // key pair table (kPairLutBytes layout, key codebook)
   float *ws_qslot;
-  float *ws_part_o;        // [B*Hkv][n_chunks][g][d]
+  float *ws_part_o;        // [B*Hkv][n_chunks][g][d]: rotated back (decode kernel) or rotated (chunk kernel)
   float *ws_part_ml;       // [B*Hkv][n_chunks][g][2]
   float *ws_qprep;         // chunk attention on the matrix cores: (q~, s) per query row
   int chunk, n_chunks;
@@ -135,7 +135,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // Scores only: the decode's key phase, writing every l_t to a.scores (no value
 // phase, no combine; the value fields are not read).
 hipError_t launch_logits(const DecodeArgs &a, hipStream_t stream);
-// The merge of the chunk partials (log-sum-exp, Pi_v^T, output; seq_inc).
+// The merge of the chunk kernel's rotated partials (log-sum-exp, Pi_v^T, output).
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
 // Chunk attention on the matrix cores: query prep, the tiles, the merge.
 hipError_t launch_chunk_mfma(const DecodeArgs &a, hipStream_t stream);
