@@ -23,8 +23,9 @@
 //  1. each wave, per 64-token tile:
 //     * scores, one token per lane: for 1- and 2-bit codes and g >= 2 a sum
 //       of table lookups, one per code nibble, each giving that nibble's
-//       partial dot product for all g heads; otherwise key codes dequantized
-//       through an LDS table times q~ from scalar registers; the sign term is
+//       partial dot product for all g heads; for 3-bit codes and g = 2, 4 one
+//       lookup per pair of codes; otherwise key codes dequantized through an
+//       LDS table times q~ from scalar registers; the sign term is
 //       a sum of table lookups, each giving 4 signs' partial sum for all g
 //       heads at once;
 //     * online softmax with a lazily raised running max;
@@ -322,6 +323,17 @@ template <int KB, int G> struct KeyTab {
   static constexpr int kFloats = kOn ? kPos * 16 * G : 1;
 };
 
+// Key scores by table for 3-bit codes and g = 2, 4: the entry (p, e, h), float
+// offset (64 p + e) g + h, is the partial dot product of q~_h with the two
+// centroids that the 6-bit index e (codes 2p, 2p + 1) encodes.  One lookup
+// and g adds replace 2 g multiply-adds.  64 KiB at g = 4; g = 8 would need
+// 128 KiB and keeps the multiply-adds.
+template <int KB, int G> struct KeyPairTab {
+  static constexpr bool kOn = KB == 3 && G >= 2 && G <= 4;
+  static constexpr int kPos = D / 2;                     // code pairs
+  static constexpr int kFloats = kOn ? kPos * 64 * G : 1;
+};
+
 // Softmax weights are exp(l - m) against a running max m that is only raised
 // when a score exceeds it by more than kLazy (then the sums and accumulators
 // are rescaled); otherwise every weight is at most e^kLazy.  The result is the
@@ -340,6 +352,7 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   constexpr int kPass = 64 * kWaves;
   constexpr int KW = D * KB / 32;   // key code words per token
   using KT = KeyTab<KB, G>;
+  using KP = KeyPairTab<KB, G>;
   constexpr int kFlight = G >= 8 ? 4 : 8;   // table positions read ahead (32 floats for g = 4, 8)
   // One block, tables first: every table lookup's address is then an index
   // plus a constant below 64 KiB, which the LDS instruction's offset field
@@ -349,7 +362,7 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
     alignas(16) float kdeq[KL::kEntries * KL::kCoords];  // key dequantization table
     // QJL sign table, entry (pos, nib, h) = sum_{k<4} s_h[4 pos + k] * (bit k of nib ? +1 : -1)
     alignas(16) float slut[QJL ? kSignLut * G : 1];
-    alignas(16) float ktab[KT::kFloats];                 // key-code tables (KeyTab)
+    alignas(16) float ktab[KT::kFloats > KP::kFloats ? KT::kFloats : KP::kFloats];   // key-code tables (KeyTab, KeyPairTab)
     alignas(16) typename Lds<G>::Shared sh;
     alignas(16) float ml[kWaves][G][2];
   };
@@ -457,7 +470,7 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
       v += sh.pro.part[pp][h][i];
       if constexpr (QJL) w += sh.pro.part_s[pp][h][i];
     }
-    if constexpr (!KT::kOn) slot[i * G + h] = v;
+    if constexpr (!KT::kOn && !KP::kOn) slot[i * G + h] = v;
     sh.pro.qr[h][i] = v;
     if constexpr (QJL) sh.pro.s[h][i] = w;
   }
@@ -482,6 +495,14 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
       for (int k = 0; k < KT::kCpn; ++k)
         v = fmaf(sh.pro.qr[h][KT::kCpn * pos + k], s_kdeq[((nib >> (KB * k)) & ((1 << KB) - 1)) * KL::kCoords], v);
       s_ktab[e] = v;
+    }
+  }
+  if constexpr (KP::kOn) {
+    // dequantization entry e holds (centroid of code e & 7, centroid of code e >> 3)
+    for (int e = tid; e < KP::kFloats; e += kThreads) {
+      const int pos = e / (64 * G), r = e % (64 * G);
+      const int n = r / G, h = r % G;
+      s_ktab[e] = fmaf(sh.pro.qr[h][2 * pos], s_kdeq[2 * n], sh.pro.qr[h][2 * pos + 1] * s_kdeq[2 * n + 1]);
     }
   }
   // The slot is re-read below through the scalar cache, which reads the L2 of
@@ -578,10 +599,24 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
           }
         }
       }
+      if constexpr (KP::kOn) {
+        // one lookup per code pair; every 8th pair's index is made to depend
+        // on the sums so far, so only 8 lookups are in flight
+#pragma unroll
+        for (int p = 0; p < KP::kPos; ++p) {
+          const int bit = 6 * p, w = bit >> 5, s_ = bit & 31;
+          uint32_t e = (s_ + 6 <= 32) ? ((kw[w] >> s_) & 63u) : (__builtin_amdgcn_alignbit(kw[w + 1], kw[w], s_) & 63u);
+          if ((p % 8) == 0) depend_v<G>(e, dot);
+          float v[G];
+          lds_load_g<G>(s_ktab + (p * 64 + e) * G, v);
+#pragma unroll
+          for (int h = 0; h < G; ++h) dot[h] += v[h];
+        }
+      }
       uniform_fptr qv = qs;
       constexpr int kRelaunder = (32 / G > KL::kCoords) ? 32 / G : KL::kCoords;
 #pragma unroll
-      for (int g = 0; g < (KT::kOn ? 0 : KL::kLookups); ++g) {
+      for (int g = 0; g < ((KT::kOn || KP::kOn) ? 0 : KL::kLookups); ++g) {
         const int c0 = g * KL::kCoords;
         if ((c0 % kRelaunder) == 0) {
           depend_s<G>(qv, snap);
