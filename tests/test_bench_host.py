@@ -1,0 +1,46 @@
+"""Host-side logic of bench.py (no GPU): the decode's vector-ALU view and the
+gate that reports counter-measured encode traffic only for the sources the
+counters were taken on."""
+import importlib.util
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_alu_peak_from_unit_counts(bench):
+    # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one fp32 FMA per lane and cycle
+    assert bench.ALU_PEAK_T_FMA == pytest.approx(256 * 4 * 16 * 2.4e9 / 1e12)
+
+
+def test_decode_alu_view(bench):
+    # the 8B layer: 32 q heads x 32768 tokens, 384 multiply-adds each, in 31 us
+    v = bench.decode_alu_view(32 * 32768, 128, 0.031)
+    assert v["algorithmic_fma_per_launch"] == 32 * 32768 * 384
+    assert v["achieved"] == pytest.approx(32 * 32768 * 384 / 31e-6 / 1e12, rel=1e-3)
+    assert v["frac"] == pytest.approx(v["achieved"] / bench.ALU_PEAK_T_FMA, rel=1e-3)
+    # MSE-only keys have no sign term: 256 per (token, q head)
+    assert bench.decode_alu_view(10, 0, 1.0)["algorithmic_fma_per_launch"] == 2560
+
+
+def test_encode_traffic_gate(bench, monkeypatch):
+    t = dict(bench.ENCODE_TRAFFIC)
+    wl = t["workload"]
+    # counters taken on the current sources are reported, for their workload only
+    monkeypatch.setattr(bench, "ENCODE_TRAFFIC", dict(t, source_sha256=bench.encode_source_sha256()))
+    assert bench.encode_traffic(wl) == t["fetch_bytes"] + t["write_bytes"]
+    assert bench.encode_traffic("another-workload") is None
+    # counters taken on other sources, or none at all, are not
+    monkeypatch.setattr(bench, "ENCODE_TRAFFIC", dict(t, source_sha256="0" * 64))
+    assert bench.encode_traffic(wl) is None
+    monkeypatch.setattr(bench, "ENCODE_TRAFFIC", dict(t, source_sha256=None))
+    assert bench.encode_traffic(wl) is None
