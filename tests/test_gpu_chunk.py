@@ -58,7 +58,8 @@ def _per_query_decode(kcb, vcb, q, kc, vc, lens):
 @pytest.mark.parametrize("kbits,m,vbits,g,n_new,qdt", [(2, 128, 3, 4, 5, "bf16"), (1, 128, 2, 8, 16, "bf16"),
                                                        (3, 128, 4, 1, 1, "bf16"), (2, 0, 2, 4, 16, "bf16"),
                                                        (4, 0, 3, 8, 5, "bf16"), (2, 128, 3, 1, 16, "f32"),
-                                                       (3, 128, 2, 2, 24, "f32"), (4, 128, 4, 2, 3, "f32")])
+                                                       (3, 128, 2, 2, 24, "f32"), (4, 128, 4, 2, 3, "f32"),
+                                                       (3, 128, 2, 4, 3, "bf16"), (3, 0, 3, 2, 5, "f32")])
 def test_chunk_parity(kbits, m, vbits, g, n_new, qdt):
     B, Hkv, t_cap = 3, 2, 1100
     lens = [1100, 3, 640]

@@ -39,7 +39,7 @@ def _nan_logits(B, Hq, t_cap):
 
 
 @pytest.mark.parametrize("kbits,m,g", [(1, 128, 4), (2, 128, 8), (3, 128, 2), (4, 128, 1),
-                                       (1, 0, 2), (2, 0, 4), (3, 0, 8), (4, 0, 1)])
+                                       (1, 0, 2), (2, 0, 4), (3, 0, 8), (4, 0, 1), (3, 128, 4), (3, 0, 4)])
 def test_logits_parity(kbits, m, g):
     B, Hkv, t_cap = 4, 2, 1300
     lens = [1300, 0, 777, 5]

@@ -167,7 +167,9 @@ def test_decode_tiny_config():
 @pytest.mark.parametrize("kbits,vbits,m,g", [(2, 3, 128, 4), (2, 2, 128, 8), (1, 1, 128, 4), (3, 4, 128, 4),
                                              (2, 3, 0, 4), (3, 2, 128, 1), (1, 4, 128, 2), (2, 1, 128, 8),
                                              # MSE-only keys (no QJL) at every width
-                                             (1, 2, 0, 8), (3, 3, 0, 2), (4, 4, 0, 4), (2, 2, 0, 1)])
+                                             (1, 2, 0, 8), (3, 3, 0, 2), (4, 4, 0, 4), (2, 2, 0, 1),
+                                             # 3-bit keys through the code-pair table (g = 2, 4)
+                                             (3, 1, 128, 2), (3, 2, 0, 4)])
 def test_decode_bit_widths_and_gqa(kbits, vbits, m, g):
     _decode_case(2, 4 * g, 4, 1300, 1300, [1300, 777], kbits, vbits, m, seed=kbits * 10 + vbits + g, outliers=4)
 
