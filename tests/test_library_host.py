@@ -16,7 +16,7 @@ T = pytest.importorskip("online_vector_quantization_amd")
 
 def _lib():
     if not os.path.exists(T.LIB_PATH):
-        pytest.fail("libtq.so is not built (run __graft_entry__.build())")
+        pytest.fail("libtq.so is not built (run python -m online_vector_quantization_amd.build)")
     return T.load_library()
 
 
