@@ -92,42 +92,54 @@ __device__ __forceinline__ float load_query(const void *q, int q_bf16, int64_t i
 
 // q~ = Pi_k q and s = (S Pi_k) q of the g query rows of one (b, kv head, j)
 // per work-group, written to rows ((b Hkv + hk) n_new + j) g + h of the prep
-// buffer.  Thread i < d holds column i of Pi_k^T, thread d + i column i of
-// (S Pi_k)^T (all reads issued before the first product), and takes the dot
-// products of all g queries: each matrix is read once per g rows.
+// buffer.  Thread (column c, part pp): c < d is column c of Pi_k^T, d + i
+// column i of (S Pi_k)^T; part pp holds entries 32 pp .. 32 pp + 31 of it
+// (all reads issued before the first product) and forms their partial dot
+// products with all g queries, which the four parts then sum in LDS.  Each
+// matrix is read once per g rows, and each thread's chain is 32 long.
+constexpr int kQpParts = 4;
+constexpr int kQpThreads = 2 * D * kQpParts;
+constexpr int kQpSpan = D / kQpParts;   // matrix entries per thread
+
 template <bool QJL, int G>
-__global__ __launch_bounds__(2 * D) void qprep_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kQpThreads) void qprep_kernel(DecodeArgs a) {
   __shared__ float sq[G][D];
+  __shared__ float part[kQpParts][G][2 * D];
   const int qrow = blockIdx.x;   // (b Hkv + hk) n_new + j
   const int j = qrow % a.n_new;
   const int bhk = qrow / a.n_new;
   const int b = bhk / a.n_kv_heads, hk = bhk % a.n_kv_heads;
   const int tid = threadIdx.x;
-  for (int e = tid; e < G * D; e += 2 * D)
+  const int col = tid & (2 * D - 1), pp = tid / (2 * D);
+  const int i = col & (D - 1);
+  const bool active = col < D || QJL;   // uniform per wave (D is a multiple of 64)
+  const float *mat = col < D ? a.rot_k_t : a.qjl_rot_t;
+  float cv[kQpSpan];
+  if (active) {
+#pragma unroll
+    for (int jj = 0; jj < kQpSpan; ++jj) cv[jj] = mat[(kQpSpan * pp + jj) * D + i];
+  }
+  for (int e = tid; e < G * D; e += kQpThreads)
     sq[e / D][e % D] =
         load_query(a.q, a.q_bf16, (static_cast<int64_t>(b * a.n_q_heads + hk * G + e / D) * a.n_new + j) * D + e % D);
-  const int i = tid & (D - 1);
-  const float *mat = tid < D ? a.rot_k_t : a.qjl_rot_t;
-  float acc[G];
+  __syncthreads();
 #pragma unroll
-  for (int h = 0; h < G; ++h) acc[h] = 0.f;
-  if (tid < D || QJL) {
-    float col[D];
+  for (int h = 0; h < G; ++h) {
+    float acc = 0.f;
+    if (active) {
 #pragma unroll
-    for (int jj = 0; jj < D; ++jj) col[jj] = mat[jj * D + i];
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int jj = 0; jj < D; ++jj) part[jj & 3] = fmaf(col[jj], sq[h][jj], part[jj & 3]);
-      acc[h] = (part[0] + part[1]) + (part[2] + part[3]);
+      for (int jj = 0; jj < kQpSpan; ++jj) acc = fmaf(cv[jj], sq[h][kQpSpan * pp + jj], acc);
     }
-  } else {
-    __syncthreads();
+    part[pp][h][col] = acc;
   }
+  __syncthreads();
+  for (int e = tid; e < G * 2 * D; e += kQpThreads) {
+    const int h = e / (2 * D), c = e % (2 * D);
+    float v = 0.f;
 #pragma unroll
-  for (int h = 0; h < G; ++h) a.ws_qprep[(static_cast<int64_t>(qrow) * G + h) * kQpStride + tid] = acc[h];
+    for (int q = 0; q < kQpParts; ++q) v += part[q][h][c];
+    a.ws_qprep[(static_cast<int64_t>(qrow) * G + h) * kQpStride + c] = v;
+  }
 }
 
 template <int KB, bool QJL>
@@ -512,9 +524,9 @@ hipError_t launch_chunk_mfma(const DecodeArgs &a, hipStream_t stream) {
 #define TQ_QP(GG)                                                                                   \
   case GG:                                                                                          \
     if (qjl)                                                                                        \
-      hipLaunchKernelGGL((qprep_kernel<true, GG>), dim3(n_qrows), dim3(2 * D), 0, stream, a);      \
+      hipLaunchKernelGGL((qprep_kernel<true, GG>), dim3(n_qrows), dim3(kQpThreads), 0, stream, a);  \
     else                                                                                            \
-      hipLaunchKernelGGL((qprep_kernel<false, GG>), dim3(n_qrows), dim3(2 * D), 0, stream, a);     \
+      hipLaunchKernelGGL((qprep_kernel<false, GG>), dim3(n_qrows), dim3(kQpThreads), 0, stream, a); \
     break;
     TQ_QP(1) TQ_QP(2) TQ_QP(4) TQ_QP(8)
 #undef TQ_QP
