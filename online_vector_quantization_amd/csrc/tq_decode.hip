@@ -37,7 +37,8 @@
 //     back by Pi_v^T (linear, so it commutes with the merge), go to the
 //     workspace.
 // A second, small launch merges the chunks of each (b, q head) (log-sum-exp)
-// and writes the output.
+// and writes the output; when every row is one chunk (and no sequence length
+// is to be advanced) the main kernel writes the output itself.
 //
 // The same kernel serves two more calls: with SC (scores only) it ends after
 // the key phase of each tile and writes every l_t (no values, no merge, no
@@ -812,6 +813,30 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
     for (int h = 0; h < G; ++h) red[(q4 * G + h) * D + i4] = r[h];
   }
   __syncthreads();
+  if (a.n_chunks == 1 && a.seq_inc == nullptr) {
+    // The row is this one chunk: normalize and write the output here (the
+    // merge launch is skipped); (1 / l) o is what it would compute for one chunk.
+    const float *red = &sh.epi.merge[0][0][0];
+    for (int e = tid; e < G * D; e += kThreads) {
+      const int h = e / D, i = e % D;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_ml[w][h][0]);
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (s_ml[w][h][0] != -INFINITY) lsum += s_ml[w][h][1] * __expf(s_ml[w][h][0] - mx);
+      const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+      const float o = fmaf(inv, red[e] + red[G * D + e] + red[2 * G * D + e] + red[3 * G * D + e], 0.f);
+      const int64_t o_idx = ((static_cast<int64_t>(b) * a.n_q_heads + hq0 + h) * a.n_new + jq) * D + i;
+      if (a.out_bf16) {
+        static_cast<uint16_t *>(a.out)[o_idx] = f32_to_bf16_rne(o);
+      } else {
+        static_cast<float *>(a.out)[o_idx] = o;
+      }
+    }
+    return;
+  }
   float *part_o = a.ws_part_o + static_cast<int64_t>(group_id) * G * D;
   {
     const float *red = &sh.epi.merge[0][0][0];
@@ -1066,7 +1091,7 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
   const hipError_t e = launch_main<false>(a, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || (a.n_chunks == 1 && a.seq_inc == nullptr)) return e;   // one chunk per row: no merge
   hipLaunchKernelGGL(combine_out_kernel, dim3(a.batch * a.n_q_heads * a.n_new), dim3(kOutThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -190,3 +190,25 @@ def test_decode_seq_len_clamped_to_capacity():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
     assert np.all(a[1].cpu().numpy() == 0.0)
+
+
+def test_decode_single_chunk_rows_write_output_in_kernel():
+    # Caches of <= 256 tokens are one token chunk per row: the main kernel writes the
+    # output itself (no merge launch). Oracle parity, and agreement with the same tokens
+    # in a longer cache that splits into several chunks and merges them.
+    B, Hkv, g, T_fill = 3, 2, 4, 200
+    rng = np.random.default_rng(44)
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, T_fill, synth.outlier_channels(rng, Hkv, 4)))
+    v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, T_fill))
+    q = H.to_device(synth.bf16_bits(rng.standard_normal((B, Hkv * g, 128)).astype(np.float32)), "bf16")
+    kcb, vcb = H.gpu_book(2, 128), H.gpu_book(3, 0)
+    seq = [200, 57, 0]
+    _log(f"decode single chunk: B={B} Hkv={Hkv} g={g} t_cap={T_fill} seq={seq}")
+    kc, vc = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, T_fill, T_fill)
+    H.check_decode(kcb, vcb, q, kc, vc, seq, 2, 3, 128)
+    kl, vl = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, 1200, T_fill)
+    sl = torch.tensor(seq, dtype=torch.int32, device=H.DEV)
+    one = T.decode_attention(kcb, vcb, q, kc, vc, sl)
+    many = T.decode_attention(kcb, vcb, q, kl, vl, sl)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(one.cpu().numpy(), many.cpu().numpy(), rtol=1e-5, atol=1e-6)
