@@ -2,15 +2,23 @@
 """Benchmark of the TurboQuant KV-cache hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input: encode every key
-and value vector of the layer into the compressed cache (two launches), then
-one decode-attention step over a full compressed cache.  Default workload:
-Llama-3-8B-shaped layer, batch 1, 32768 tokens, 32 q heads / 8 KV heads,
-head_dim 128, keys b=3 (2-bit codes + 1-bit QJL, m=128), values 3-bit.
+and value vector of the workload into the compressed cache (two launches),
+then one decode-attention step over a compressed cache.
+
+Default run (no flags): the headline line is the largest single-GPU workload,
+the prefill-scale bulk encode (16,777,216 bf16 K and V vectors of dim 128;
+keys b=4 = 3-bit codes + 1-bit QJL with m=128, values 4-bit), then 64 q heads
+(8 per KV head) decoding over a 262,144-token x 8-head view of the cache.  The
+other workloads ride along as nested sub-records under "configs": the tiny
+quality case, the Llama-3-8B-shaped layer, the batched decode at b=2 and b=4
+with its 8-step append loop, and the Llama-3-70B-shaped long context.
+`--config NAME` runs one workload as the headline alone.
 
 Inputs are resident in HBM before timing.  To keep the 256 MB Infinity Cache
-from serving re-reads, each step reads one of several input replicas and the
-decode reads a cache replica written many steps earlier (>= 1 GiB of distinct
-caches in rotation); --hot disables the rotation.
+from serving re-reads, the layer workloads read one of several input replicas
+per step and decode a cache replica written many steps earlier (>= 1 GiB of
+distinct caches in rotation; --hot disables it); the bulk workload's 8.6 GB of
+inputs and 294 MB decode view exceed it by themselves.
 
 Prints ONE JSON line.  `value` is the decode-attention throughput in GB/s of
 compressed K+V bytes read; encode throughput (Mvectors/s) and both kernels'
@@ -38,20 +46,34 @@ HBM_PEAK_GBPS = 8000.0
 # bytes to what the same counter read for it.  Valid only for the encode
 # sources they were taken on (sha256 over tq_encode.hip and tq_encode_body.inc,
 # below); otherwise reported as null.
-ENCODE_TRAFFIC = {"source_sha256": "d6229989d1b4806eb7617f864ab0e949205112be30e940cbffb24cf6b395f4f0",
-                  "workload": "llama3-8b-layer-b1-s32768",
-                  "fetch_bytes": 68507571, "write_bytes": 14710275}
+# Per workload: the key-encode launch's HBM bytes and its matrix-core / vector
+# busy fractions (SQ_VALU_MFMA_BUSY_CYCLES over 1,024 SIMDs x kernel cycles;
+# SQ_ACTIVE_INST_VALU less MFMA instructions at 4 cycles each).
+ENCODE_COUNTERS = {
+    "llama3-8b-layer-b1-s32768": {"source_sha256": "d6229989d1b4806eb7617f864ab0e949205112be30e940cbffb24cf6b395f4f0",
+                                  "fetch_bytes": 68507571, "write_bytes": 14710275,
+                                  "mfma_busy": 0.338, "valu_busy": 0.336},
+}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+BULK_NAME = "bulk-encode-16777216-kv-then-decode-g8-s262144"
 METRIC = "decode-attn HBM GB/s (% of peak) on compressed KV; encode Mvectors/s"
+# "dtype" names the arithmetic: fp32 accumulation throughout (the matrix-core
+# products take bf16 hi/lo operand splits, three products per fp32 product);
+# the data crossing the boundary are bf16 (fp32 for the tiny workload).
+DTYPES = {"input": "bf16", "query": "bf16", "output": "bf16", "accumulate": "f32",
+          "mfma_operands": "bf16 hi/lo split of fp32 values"}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama8b", choices=["llama8b", "llama70b", "batched2", "batched4", "bulk", "tiny"],
-                    help="bulk: encode 16,777,216 K and V vectors, then 64 queries over a 262144 x 8 view")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="all",
+                    choices=["all", "llama8b", "llama70b", "batched2", "batched4", "bulk", "tiny"],
+                    help="all (default): the bulk workload as the headline plus every other workload as a "
+                         "sub-record; bulk: encode 16,777,216 K and V vectors, then 64 queries over a "
+                         "262144 x 8 view")
     ap.add_argument("--hot", action="store_true", help="no replica rotation (cache-resident numbers)")
     ap.add_argument("--append-steps", type=int, default=0, metavar="N",
                     help="also time N decode-loop steps (append one token per sequence and head, then attend): "
@@ -93,14 +115,47 @@ def main():
         sys.exit(1)
     T.load_library()
     dev = torch.device("cuda", 0)
+    if args.config == "all":
+        line = bench_bulk(args, T, dev, cpu=not args.no_cpu_baseline)
+        subs = {}
+        for name in ("tiny", "llama8b", "batched2", "batched4", "llama70b"):
+            t0 = time.time()
+            if name == "tiny":
+                rec = bench_tiny(args, T, dev)
+            else:
+                rec = bench_layer(args, T, dev, name, append_steps=8 if name.startswith("batched") else 0,
+                                  chunk=args.chunk if name == "llama8b" else 0, logits=True, cpu=False)
+            subs[name] = sub_record(rec)
+            print(f"[bench] sub-record {name} done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        line["configs"] = subs
+        print(json.dumps(line), flush=True)
+        return
     if args.config == "bulk":
-        print(json.dumps(bench_bulk(args, T, dev)), flush=True)
+        print(json.dumps(bench_bulk(args, T, dev, cpu=not args.no_cpu_baseline)), flush=True)
         return
     if args.config == "tiny":
         print(json.dumps(bench_tiny(args, T, dev)), flush=True)
         return
+    line = bench_layer(args, T, dev, args.config, append_steps=args.append_steps, chunk=args.chunk, logits=True,
+                       cpu=not args.no_cpu_baseline)
+    print(json.dumps(line), flush=True)
+
+
+# keys of a full line that a nested sub-record leaves out (the headline carries them)
+_SUB_DROP = ("metric", "unit", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data", "steps", "warmup")
+
+
+def sub_record(line):
+    """A workload's line as a nested sub-record of the headline line."""
+    return {k: v for k, v in line.items() if k not in _SUB_DROP}
+
+
+def bench_layer(args, T, dev, name, append_steps=0, chunk=0, logits=True, cpu=True):
+    """One layer-shaped workload (8B, batched, 70B): encode all of its K and V,
+    then one decode over a full cache replica, per step."""
+    import torch
     t0 = time.time()
-    wl = workload(args.config)
+    wl = workload(name)
     B, Hq, Hkv, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.seq_len
     kbits_mse = wl.k_bits - 1
     print(f"[bench] workload {wl.name}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -193,7 +248,6 @@ def main():
     enc_v_bytes = n_vec * (256 + v_rec)
     enc_k_gbps = enc_k_bytes / (enc_k.mean() * 1e-3) / 1e9
     enc_v_gbps = enc_v_bytes / (enc_v.mean() * 1e-3) / 1e9
-    enc_k_tflops = n_vec * 2 * 128 * (128 + qjl_m) / (enc_k.mean() * 1e-3) / 1e12
 
     line = {
         "metric": METRIC,
@@ -207,6 +261,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtypes": DTYPES,
         "data": "synthetic",
         "config": {
             "workload": wl.name, "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
@@ -224,7 +279,7 @@ def main():
             "achieved": round(enc_k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4), "traffic": encode_traffic(wl.name) if qjl_m else None,
             "algorithmic_bytes_per_launch": enc_k_bytes, "avg_launch_us": round(float(enc_k.mean()) * 1e3, 2),
-            "mfma_tflops_algorithmic": round(enc_k_tflops, 1),
+            "mfma": key_encode_mfma(n_vec, qjl_m, True, float(enc_k.mean()), wl.name),
         },
         "roofline_values_encode": {
             "bound": "hbm", "achieved": round(enc_v_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -245,17 +300,19 @@ def main():
             for name, arr in (("encode_keys", enc_k), ("encode_values", enc_v), ("decode", dec))},
         "copy_gbps_context": copy_bandwidth(dev),
     }
-    line["attention_logits"] = logits_only(T, kcb, q, caches, seq, ws, n_vec * k_rec, B * Hq * S * 4, args, dev)
-    if args.chunk > 0:
-        line["chunk_attention"] = chunk_only(T, kcb, vcb, caches, S, Hq, args, dev)
-    if args.append_steps > 0:
-        line["append_step_us"] = append_steps(wl, kcb, vcb, up, args.append_steps, dev)
-    if not args.no_cpu_baseline:
+    if logits:
+        line["attention_logits"] = logits_only(T, kcb, q, caches, seq, ws, n_vec * k_rec, B * Hq * S * 4, args, dev)
+    if chunk > 0:
+        line["chunk_attention"] = chunk_only(T, kcb, vcb, caches, S, Hq, chunk, args, dev)
+    del caches, ins
+    if append_steps > 0:
+        line["append_step_us"] = run_append_steps(wl, kcb, vcb, up, append_steps, dev)
+    if cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, qjl=bool(qjl_m))
-    print(json.dumps(line), flush=True)
+    return line
 
 
-def bench_bulk(args, T, dev):
+def bench_bulk(args, T, dev, cpu=True):
     """Prefill-scale bulk encode: every step encodes 16,777,216 K vectors (b' = 3
     + QJL) and 16,777,216 V vectors (4-bit), then decodes 64 q heads (8 per kv
     head) over the first 2,097,152 rows of each cache viewed as [1, 8, 262144].
@@ -321,8 +378,8 @@ def bench_bulk(args, T, dev):
     line = {
         "metric": METRIC, "value": round(dec_gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(start.elapsed_time(end) / steps, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "bulk-encode-16777216-kv-then-decode-g8-s262144", "vectors": n, "key_bits": 4,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "dtypes": DTYPES, "data": "synthetic",
+        "config": {"workload": BULK_NAME, "vectors": n, "key_bits": 4,
                    "value_bits": 4, "qjl_dim": 128, "decode_view": [1, Hkv, Tlen], "q_heads": Hq,
                    "input_dtype": "bf16", "key_mode": "(b-1)-bit codes + 1-bit QJL",
                    "step": "encode all K and V vectors, then one decode step over the view"},
@@ -332,15 +389,16 @@ def bench_bulk(args, T, dev):
         "encode_us": {"keys": round(float(enc_k.mean()) * 1e3, 1), "values": round(float(enc_v.mean()) * 1e3, 1)},
         "roofline": {"kernel": "encode (keys: rotation + QJL)", "bound": "hbm", "achieved": round(enc_k_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": enc_k_bytes,
-                     "avg_launch_us": round(float(enc_k.mean()) * 1e3, 1)},
+                     "traffic": encode_traffic(BULK_NAME), "algorithmic_bytes_per_launch": enc_k_bytes,
+                     "avg_launch_us": round(float(enc_k.mean()) * 1e3, 1),
+                     "mfma": key_encode_mfma(n, 128, True, float(enc_k.mean()), BULK_NAME)},
         "roofline_values_encode": {"bound": "hbm", "achieved": round(enc_v_bytes / (enc_v.mean() * 1e-3) / 1e9, 1),
                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "algorithmic_bytes_per_launch": enc_v_bytes},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": dec_bytes,
                             "alu": decode_alu_view(Hq * Tlen, 128, float(dec.mean()))},
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         line["cpu_baseline"] = cpu_baseline_bulk(kx, vx, q, args.cpu_seconds)
     return line
 
@@ -391,7 +449,7 @@ def bench_tiny(args, T, dev):
     return {
         "metric": METRIC, "value": round(dec_gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(float((enc + dec).mean()), 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "dtypes": dict(DTYPES, input="f32", query="f32", output="f32"), "data": "synthetic",
         "config": {"workload": wl.name, "keys": n, "head_dim": 128, "key_bits": 3, "qjl_dim": 128,
                    "input_dtype": "f32", "step": "encode the keys (and the same vectors as 2-bit values), then decode"},
         "encode_us": round(float(enc.mean()) * 1e3, 2), "decode_us": round(float(dec.mean()) * 1e3, 2),
@@ -515,12 +573,11 @@ def logits_only(T, kcb, q, caches, seq, ws, key_bytes, logit_bytes, args, dev):
             "key_record_bytes": key_bytes, "logit_bytes": logit_bytes}
 
 
-def chunk_only(T, kcb, vcb, caches, S, Hq, args, dev):
-    """Causal attention of args.chunk new queries per (b, q head), the last
+def chunk_only(T, kcb, vcb, caches, S, Hq, n_new, args, dev):
+    """Causal attention of n_new new queries per (b, q head), the last
     positions of a full cache, over the same cold cache replicas: mean time per
     launch pair and the cache bytes per launch (each query block re-reads them)."""
     import torch
-    n_new = args.chunk
     stream = torch.cuda.current_stream(dev)
     kc0, vc0 = caches[0]
     B = kc0.codes.shape[0]
@@ -564,7 +621,7 @@ def chunk_only(T, kcb, vcb, caches, S, Hq, args, dev):
     return res
 
 
-def append_steps(wl, kcb, vcb, up, steps, dev):
+def run_append_steps(wl, kcb, vcb, up, steps, dev):
     """Per-step time of a decode loop over the workload's caches (prefilled with
     seq_len tokens, capacity seq_len + steps): each step appends one key and
     value per (sequence, kv head) and attends the step's queries over the grown
@@ -646,15 +703,37 @@ def append_steps(wl, kcb, vcb, up, steps, dev):
     return res
 
 
+def encode_counters(workload_name):
+    """Counter figures of one key-encode launch on this workload, or None when
+    they are missing or the encode source changed since they were taken."""
+    t = ENCODE_COUNTERS.get(workload_name)
+    if t is None or encode_source_sha256() != t["source_sha256"]:
+        return None
+    return t
+
+
 def encode_traffic(workload_name):
-    """Counter-measured HBM bytes of one key-encode launch, or None when the
-    figures are missing or the encode source changed since they were taken."""
-    t = ENCODE_TRAFFIC
-    if t["source_sha256"] is None or workload_name != t["workload"]:
-        return None
-    if encode_source_sha256() != t["source_sha256"]:
-        return None
-    return t["fetch_bytes"] + t["write_bytes"]
+    """Counter-measured HBM bytes of one key-encode launch (FETCH_SIZE + WRITE_SIZE, scaled), or None."""
+    t = encode_counters(workload_name)
+    return None if t is None else t["fetch_bytes"] + t["write_bytes"]
+
+
+def key_encode_mfma(n_vec, qjl_m, x_bf16, ms, workload_name):
+    """The key encode against the bf16 matrix-core peak: algorithmic flops
+    (2 d^2 for the rotation + 2 m d for the QJL product per vector) and flops
+    as issued by the hi/lo operand splits (rotation: 2 products per product for
+    bf16 input, 3 for fp32; QJL: 3), plus the counters' busy fractions."""
+    alg = n_vec * 2.0 * 128 * (128 + qjl_m)
+    rot_passes = 2 if x_bf16 else 3
+    issued = n_vec * 2.0 * 128 * (rot_passes * 128 + 3 * qjl_m)
+    sec = ms * 1e-3
+    c = encode_counters(workload_name)
+    return {"bound": "mfma", "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "achieved_algorithmic": round(alg / sec / 1e12, 1), "frac_algorithmic": round(alg / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "achieved_issued": round(issued / sec / 1e12, 1), "frac_issued": round(issued / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "flops_per_launch_algorithmic": alg, "flops_per_launch_issued": issued,
+            "counters_mfma_busy": None if c is None else c["mfma_busy"],
+            "counters_valu_busy": None if c is None else c["valu_busy"]}
 
 
 def encode_source_sha256():

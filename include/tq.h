@@ -172,6 +172,23 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
                               tq_dtype out_dtype, float *dbg_scores, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* tq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Its scratch is a static device array of
+ * 16 MiB inside the library, one copy per GPU, held until the process ends;
+ * this call itself calls no hipMalloc, hipFree or other allocating routine.
+ * Arguments, results and errors are those of tq_decode_attention (same kernels,
+ * bitwise the same output), except that sizes whose workspace
+ * (tq_decode_workspace_bytes) exceeds 16 MiB return TQ_ERR_INVALID_ARG and
+ * launch nothing.  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must be
+ * serialized by the caller.  The scratch's contents on entry do not matter. */
+tq_status tq_decode_attention_static(const tq_codebook *kcb, const tq_codebook *vcb, const void *q,
+                                     tq_dtype q_dtype, const tq_cache *k, const tq_cache *v,
+                                     const int32_t *seq_len, int32_t batch, int32_t n_q_heads,
+                                     int32_t n_kv_heads, float softmax_scale, void *out, tq_dtype out_dtype,
+                                     float *dbg_scores, void *stream);
+
 /* Attention of a chunk of n_new new tokens' queries over the compressed cache
  * (chunked prefill, or several decode tokens verified at once), each query
  * causal: query j of sequence b sits at position p = seq_len[b] - n_new + j

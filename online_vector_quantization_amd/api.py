@@ -7,7 +7,6 @@ streams.  If libtq.so has not been built, every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -24,7 +23,7 @@ TQ_F32, TQ_BF16 = 0, 1
 EXPORTED = (
     "tq_codebook_build", "tq_codebook_free", "tq_codebook_info", "tq_codebook_export",
     "tq_codebook_export_f64", "tq_record_words", "tq_encode_kv", "tq_decode_workspace_bytes",
-    "tq_decode_attention", "tq_append_decode", "tq_attention_logits", "tq_chunk_attention",
+    "tq_decode_attention", "tq_decode_attention_static", "tq_append_decode", "tq_attention_logits", "tq_chunk_attention",
     "tq_chunk_workspace_bytes", "tq_status_string", "tq_last_error",
 )
 
@@ -63,6 +62,8 @@ def load_library() -> ctypes.CDLL:
     lib.tq_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_decode_attention.argtypes = [vp, vp, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache), vp,
                                         i32, i32, i32, f32, vp, i32, vp, vp, ctypes.c_size_t, vp]
+    lib.tq_decode_attention_static.argtypes = [vp, vp, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache),
+                                               vp, i32, i32, i32, f32, vp, i32, vp, vp]
     lib.tq_append_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, ctypes.POINTER(TqCache), ctypes.POINTER(TqCache),
                                      vp, i32, i32, i32, f32, vp, i32, vp, ctypes.c_size_t, vp]
     lib.tq_chunk_workspace_bytes.argtypes = [i32, i32, i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -278,6 +279,28 @@ def decode_attention(kcb: Codebook, vcb: Codebook, q: torch.Tensor, kcache: Comp
     return out
 
 
+def decode_attention_static(kcb: Codebook, vcb: Codebook, q: torch.Tensor, kcache: CompressedCache,
+                            vcache: CompressedCache, seq_len: torch.Tensor, out: Optional[torch.Tensor] = None,
+                            softmax_scale: float = 0.0, out_dtype=torch.float32,
+                            dbg_scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tq_decode_attention_static: decode_attention with the library's static scratch (no workspace)."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, d] tensor")
+    B, Hq, d = q.shape
+    Hkv = kcache.codes.shape[1]
+    if seq_len.dtype != torch.int32 or seq_len.numel() != B or not seq_len.is_contiguous():
+        raise ValueError("seq_len must be a contiguous int32 tensor with B entries")
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=out_dtype, device=q.device)
+    _require_cuda(q, seq_len, out, dbg_scores, kcache.codes, vcache.codes)
+    ks, vs = kcache.as_struct(), vcache.as_struct()
+    _check(load_library().tq_decode_attention_static(
+        kcb.handle, vcb.handle, _ptr(q), _dtype_code(q), ctypes.byref(ks), ctypes.byref(vs), _ptr(seq_len),
+        B, Hq, Hkv, float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(dbg_scores),
+        _stream_handle(stream, q.device)), "tq_decode_attention_static")
+    return out
+
+
 def chunk_attention(kcb: Codebook, vcb: Codebook, q: torch.Tensor, kcache: CompressedCache,
                     vcache: CompressedCache, seq_len: torch.Tensor, out: Optional[torch.Tensor] = None,
                     softmax_scale: float = 0.0, out_dtype=torch.float32, workspace: Optional[torch.Tensor] = None,
@@ -369,7 +392,3 @@ def compressed_bytes_per_token(kcb: Codebook, vcb: Codebook) -> int:
 def chunk_uses_mfma(g: int, n_new: int) -> bool:
     """Whether tq_chunk_attention takes its matrix-core kernel (16 or more query rows per kv head)."""
     return g * n_new >= 16
-
-
-def qjl_coefficient(m: int) -> float:
-    return math.sqrt(math.pi / 2.0) / m

@@ -15,6 +15,14 @@
 #include "tq_internal.h"
 #include "tq_kernels.h"
 
+// Scratch of tq_decode_attention_static, for callers that cannot allocate:
+// one copy of this array per GPU, loaded with the code object and held until
+// the process ends.  On the host `scratch` names a stand-in, not the device
+// copy: host code only ever uses the address hipGetSymbolAddress returns for
+// the current device (scratch_address below).
+constexpr size_t kStaticScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -67,6 +75,31 @@ int cu_count(int device) {
 }
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_addr;   // per device ordinal; null until resolved
+
+// Device address of `scratch` on `device`, resolved once per device with that
+// device current (codebook set-up does it; the entry point's first call on a
+// device otherwise).  Allocates nothing on the GPU.
+tq_status scratch_address(int device, void **out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (device < 0) return fail(TQ_ERR_INVALID_ARG, "scratch needs a GPU device");
+  if (device < static_cast<int>(g_scratch_addr.size()) && g_scratch_addr[device] != nullptr) {
+    *out = g_scratch_addr[device];
+    return ok();
+  }
+  DeviceGuard guard(device);
+  if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice(%d): %s", device, hipGetErrorString(guard.err));
+  void *p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || p == nullptr)
+    return fail(TQ_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", device, hipGetErrorString(e));
+  if (device >= static_cast<int>(g_scratch_addr.size())) g_scratch_addr.resize(device + 1, nullptr);
+  g_scratch_addr[device] = p;
+  *out = p;
+  return ok();
+}
 
 tq_status upload_tables(tq_codebook *cb) {
   const tq::HostTables &h = cb->host;
@@ -178,6 +211,8 @@ tq_status tq_codebook_build(int32_t head_dim, int32_t mse_bits, int32_t qjl_dim,
   cb->device = device;
   if (device >= 0) {
     tq_status s = upload_tables(cb);
+    void *scr = nullptr;
+    if (s == TQ_OK) s = scratch_address(device, &scr);   // set-up of the allocation-free decode
     if (s != TQ_OK) {
       tq_codebook_free(cb);
       return s;
@@ -448,6 +483,29 @@ tq_status tq_decode_attention(const tq_codebook *kcb, const tq_codebook *vcb, co
   tq::DecodeArgs a{};
   const tq_status st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, 1,
                                       softmax_scale, out, out_dtype, dbg_scores, workspace, workspace_bytes, &a);
+  if (st != TQ_OK) return st;
+  return run_decode(kcb, a, stream);
+}
+
+tq_status tq_decode_attention_static(const tq_codebook *kcb, const tq_codebook *vcb, const void *q,
+                                     tq_dtype q_dtype, const tq_cache *k, const tq_cache *v, const int32_t *seq_len,
+                                     int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, float softmax_scale,
+                                     void *out, tq_dtype out_dtype, float *dbg_scores, void *stream) {
+  if (kcb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  if (kcb->device < 0) return fail(TQ_ERR_INVALID_ARG, "the codebook must live on a GPU device");
+  if (k == nullptr) return fail(TQ_ERR_INVALID_ARG, "NULL argument");
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0 || k->t_cap < 1)
+    return fail(TQ_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d/%d)", batch, n_q_heads, n_kv_heads);
+  const size_t need = tq::plan_decode(batch, n_q_heads, n_kv_heads, k->t_cap).total_bytes;
+  if (need > kStaticScratchBytes)
+    return fail(TQ_ERR_INVALID_ARG, "these sizes need %zu bytes of scratch; the static scratch holds %zu", need,
+                kStaticScratchBytes);
+  void *scr = nullptr;
+  tq_status st = scratch_address(kcb->device, &scr);
+  if (st != TQ_OK) return st;
+  tq::DecodeArgs a{};
+  st = prepare_decode(kcb, vcb, q, q_dtype, k, v, seq_len, batch, n_q_heads, n_kv_heads, 1, softmax_scale, out,
+                      out_dtype, dbg_scores, scr, kStaticScratchBytes, &a);
   if (st != TQ_OK) return st;
   return run_decode(kcb, a, stream);
 }

@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // ---- 4. online softmax, 4 threads per row
+    // ---- 4. online softmax, kSmT (8) threads per row
     {
       float lv[16];
 #pragma unroll

@@ -509,6 +509,11 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   // The slot is re-read below through the scalar cache, which reads the L2 of
   // this work-group's own XCD (and was invalidated at kernel start): waiting
   // for this wave's stores to complete is enough; no device-wide write-back.
+  // This holds only while (1) no other work-group of the launch writes this
+  // slot (launch_main checks that the grid gives every work-group its own
+  // 64-byte aligned slot), (2) no scalar load of the slot happens before these
+  // stores (the main loop's first use of qs goes through depend_s on values
+  // computed after this point, which keeps the compiler from hoisting it).
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -1035,10 +1040,26 @@ hipError_t launch_q(const DecodeArgs &a, int g, dim3 grid, hipStream_t stream) {
   return a.qjl_m > 0 ? launch_g<KB, true, SC>(a, g, grid, stream) : launch_g<KB, false, SC>(a, g, grid, stream);
 }
 
+// Work-group (chunk, kv head x query, batch) of the grid below owns q~ slot
+// group_id = ((b Hkv + hk) n_new + j) n_chunks + chunk: one slot each, g * d
+// floats at g * d * 4 bytes apart from a 64-byte aligned base, so no two
+// work-groups of a launch share a cache line of the slots (the main loop
+// re-reads its own slot through the scalar cache, which is coherent only with
+// this work-group's own completed stores).
+bool qslots_disjoint(const DecodeArgs &a, int g) {
+  static_assert((kHeadDim * sizeof(float)) % 64 == 0, "a slot spans whole 64-byte lines");
+  if (reinterpret_cast<uintptr_t>(a.ws_qslot) % 64 != 0) return false;
+  const int64_t groups = static_cast<int64_t>(a.batch) * a.n_kv_heads * a.n_new * a.n_chunks;
+  const uintptr_t end = reinterpret_cast<uintptr_t>(a.ws_qslot) + static_cast<uintptr_t>(groups) * g * kHeadDim * 4;
+  // the slots end before the partial outputs begin (the plan's layout)
+  return a.ws_part_o == nullptr || end <= reinterpret_cast<uintptr_t>(a.ws_part_o);
+}
+
 template <bool SC>
 hipError_t launch_main(const DecodeArgs &a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
   if (a.n_chunks > kMaxDecodeChunks || a.n_new < 1 || a.n_kv_heads * a.n_new > 65535) return hipErrorInvalidValue;
+  if (!qslots_disjoint(a, g)) return hipErrorInvalidValue;
   const dim3 grid(a.n_chunks, a.n_kv_heads * a.n_new, a.batch);
   switch (a.k_bits) {
     case 1: return launch_q<1, SC>(a, g, grid, stream);

@@ -33,14 +33,31 @@ def test_decode_alu_view(bench):
 
 
 def test_encode_traffic_gate(bench, monkeypatch):
-    t = dict(bench.ENCODE_TRAFFIC)
-    wl = t["workload"]
+    wl, t = next(iter(bench.ENCODE_COUNTERS.items()))
     # counters taken on the current sources are reported, for their workload only
-    monkeypatch.setattr(bench, "ENCODE_TRAFFIC", dict(t, source_sha256=bench.encode_source_sha256()))
+    monkeypatch.setattr(bench, "ENCODE_COUNTERS", {wl: dict(t, source_sha256=bench.encode_source_sha256())})
     assert bench.encode_traffic(wl) == t["fetch_bytes"] + t["write_bytes"]
     assert bench.encode_traffic("another-workload") is None
+    assert bench.key_encode_mfma(1000, 128, True, 1.0, wl)["counters_mfma_busy"] == t["mfma_busy"]
     # counters taken on other sources, or none at all, are not
-    monkeypatch.setattr(bench, "ENCODE_TRAFFIC", dict(t, source_sha256="0" * 64))
+    monkeypatch.setattr(bench, "ENCODE_COUNTERS", {wl: dict(t, source_sha256="0" * 64)})
     assert bench.encode_traffic(wl) is None
-    monkeypatch.setattr(bench, "ENCODE_TRAFFIC", dict(t, source_sha256=None))
+    assert bench.key_encode_mfma(1000, 128, True, 1.0, wl)["counters_mfma_busy"] is None
+    monkeypatch.setattr(bench, "ENCODE_COUNTERS", {})
     assert bench.encode_traffic(wl) is None
+
+
+def test_key_encode_mfma_flops(bench):
+    # 10^7 bf16 keys with m = 128 in 1 ms: 2 d (d + m) algorithmic flops per key;
+    # issued, the rotation takes 2 bf16 products per product and the QJL 3
+    n = 10 ** 7
+    v = bench.key_encode_mfma(n, 128, True, 1.0, "none")
+    assert v["flops_per_launch_algorithmic"] == n * 2 * 128 * 256
+    assert v["flops_per_launch_issued"] == n * 2 * 128 * (2 * 128 + 3 * 128)
+    assert v["achieved_issued"] == pytest.approx(n * 2 * 128 * 640 / 1e-3 / 1e12, rel=1e-3)
+    assert bench.key_encode_mfma(1000, 0, False, 1.0, "none")["flops_per_launch_issued"] == 1000 * 2 * 128 * 3 * 128
+
+
+def test_sub_record_drops_headline_keys(bench):
+    line = {"metric": "m", "value": 1.0, "unit": "GB/s", "config": {"workload": "w"}, "steps": 3}
+    assert bench.sub_record(line) == {"value": 1.0, "config": {"workload": "w"}}

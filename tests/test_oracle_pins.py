@@ -317,6 +317,43 @@ def test_encode_keys_residual_and_signs():
     assert np.all(np.abs(e["r"]) <= np.max(np.diff(np.concatenate(([-1], t, [1])))))
 
 
+def test_residual_from_rotated_hand_worked_d4():
+    # d = 4, one bit: the centroids are -+4/(3 pi) (closed form, pinned above) and
+    # the threshold is 0.  y = (0.5, -0.1, 0.3, -0.7) quantizes to (1, 0, 1, 0),
+    # so r = (0.5 - c, -0.1 + c, 0.3 - c, -0.7 + c) with c = 0.42441318157838756
+    # (values written out by hand below) and gamma = sqrt(sum r_j^2).
+    c = np.array([-4.0 / (3.0 * math.pi), 4.0 / (3.0 * math.pi)])
+    y = np.array([[0.5, -0.1, 0.3, -0.7]])
+    idx = O.quantize(y, np.array([0.0]))
+    np.testing.assert_array_equal(idx, [[1, 0, 1, 0]])
+    r, gamma = O.residual_from_rotated(y, idx, c)
+    np.testing.assert_allclose(r, [[0.07558681842161241, 0.3244131815783876, -0.1244131815783876,
+                                    -0.27558681842161237]], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(gamma, [0.44987110791772045], rtol=1e-15)
+
+
+def test_residual_from_rotated_mean_square_is_distortion():
+    # Over uniform unit vectors (Gaussian draws normalized; a rotation leaves
+    # that law unchanged), E[gamma^2] = E||y - c[idx]||^2 is the codebook's
+    # distortion D, which is pinned to quadrature and to closed forms above.
+    # The function also equals encode()'s own residual on the same rows.
+    d = 128
+    rng = np.random.default_rng(21)
+    g = rng.standard_normal((20000, d))
+    y = g / np.linalg.norm(g, axis=1, keepdims=True)
+    for bits in (1, 2, 3):
+        c, t = O.build_codebook(d, bits)
+        idx = O.quantize(y, t)
+        r, gamma = O.residual_from_rotated(y, idx, c)
+        D = O.codebook_distortion(d, c.astype(np.float64), t.astype(np.float64))
+        g2 = gamma * gamma
+        assert abs(g2.mean() - D) < 3.0 * g2.std() / math.sqrt(g2.size)
+        e = O.encode(y[:200], np.eye(d), c, t, O.qjl_matrix(32, d, 3))
+        r2, gamma2 = O.residual_from_rotated(e["y"], e["idx"], c)
+        np.testing.assert_allclose(r2, e["r"], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(gamma2, e["gamma"], rtol=1e-14)
+
+
 # ---------------------------------------------------------------- QJL estimator
 
 def test_qjl_unbiased_1e5_trials():
