@@ -76,6 +76,45 @@ int cu_count(int device) {
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
+// IEEE binary16 bits of a float, round to nearest even (normal and subnormal
+// results; the tables only hold finite values well inside the range).
+uint16_t f16_bits_rne(float v) {
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t au = u & 0x7fffffffu;
+  if (au >= 0x47800000u) return static_cast<uint16_t>(sign | 0x7c00u);   // overflow -> inf
+  if (au < 0x38800000u) {                                                  // subnormal or zero
+    float a;
+    std::memcpy(&a, &au, 4);
+    const float scaled = a * 16777216.0f;   // a / 2^-24
+    const uint32_t q = static_cast<uint32_t>(std::nearbyint(scaled));
+    return static_cast<uint16_t>(sign | q);
+  }
+  const uint32_t mant = au & 0x7fffffu;
+  const int32_t exp = static_cast<int32_t>(au >> 23) - 127 + 15;
+  uint32_t h = (static_cast<uint32_t>(exp) << 10) | (mant >> 13);
+  const uint32_t rem = mant & 0x1fffu;
+  if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ++h;   // carries into the exponent correctly
+  return static_cast<uint16_t>(sign | h);
+}
+
+float f16_bits_to_float(uint16_t b) {
+  const uint32_t sign = (b & 0x8000u) << 16, e = (b >> 10) & 0x1fu, m = b & 0x3ffu;
+  float r;
+  if (e == 0) {
+    r = std::ldexp(static_cast<float>(m), -24);
+    uint32_t u;
+    std::memcpy(&u, &r, 4);
+    u |= sign;
+    std::memcpy(&r, &u, 4);
+    return r;
+  }
+  const uint32_t u = sign | ((e + 112u) << 23) | (m << 13);
+  std::memcpy(&r, &u, 4);
+  return r;
+}
+
 std::mutex g_scratch_mu;
 std::vector<void *> g_scratch_addr;   // per device ordinal; null until resolved
 
@@ -126,6 +165,12 @@ tq_status upload_tables(tq_codebook *cb) {
   off = align256(off + tq::kPairLutBytes);
   cb->off_qcells = off;
   off = align256(off + tq::kQuantCellEntries * 4 * sizeof(float));
+  cb->off_mkey_lut = off;
+  off = align256(off + tq::kMKeyLutBytes);
+  cb->off_mval_lut = off;
+  off = align256(off + tq::kMValLutBytes);
+  cb->off_sign_lut = off;
+  off = align256(off + tq::kSignLutBytes);
   cb->dev_bytes = off;
 
   std::vector<unsigned char> img(off, 0);
@@ -148,6 +193,38 @@ tq_status upload_tables(tq_codebook *cb) {
           v += h.qjl64[static_cast<size_t>(r) * d + j] * h.rotation64[static_cast<size_t>(j) * d + i];
         st[i * m + r] = static_cast<float>(v);
       }
+  }
+  {
+    // Matrix-core decode operand tables (layouts in tq_kernels.h): centroid
+    // value c as (hi, lo) = (bf16(c), bf16(c - hi)), two per 32-bit word.
+    const int b = h.bits, mask = (1 << b) - 1;
+    std::vector<uint16_t> hi(h.levels), lo(h.levels);
+    for (int k = 0; k < h.levels; ++k) {
+      hi[k] = tq::bf16_bits_rne(h.centroids[k]);
+      lo[k] = tq::bf16_bits_rne(h.centroids[k] - tq::bf16_bits_to_float(hi[k]));
+    }
+    auto pair = [](uint16_t x, uint16_t y) { return static_cast<uint32_t>(x) | (static_cast<uint32_t>(y) << 16); };
+    // keys: fp16 (hi, lo) of 256 c (the score products run in fp16)
+    std::vector<uint16_t> khi(h.levels), klo(h.levels);
+    for (int k = 0; k < h.levels; ++k) {
+      const float x = 256.0f * h.centroids[k];
+      khi[k] = f16_bits_rne(x);
+      klo[k] = f16_bits_rne(x - f16_bits_to_float(khi[k]));
+    }
+    uint32_t *mk = reinterpret_cast<uint32_t *>(img.data() + cb->off_mkey_lut);
+    uint32_t *mv = reinterpret_cast<uint32_t *>(img.data() + cb->off_mval_lut);
+    for (int e = 0; e < (1 << (2 * b)); ++e) {
+      const int c0 = e & mask, c1 = (e >> b) & mask;
+      mk[2 * e] = pair(khi[c0], klo[c0]);
+      mk[2 * e + 1] = pair(khi[c1], klo[c1]);
+      mv[2 * e] = pair(hi[c0], lo[c0]);   // values: bf16 (hi, lo) of c
+      mv[2 * e + 1] = pair(hi[c1], lo[c1]);
+    }
+    uint32_t *sg = reinterpret_cast<uint32_t *>(img.data() + cb->off_sign_lut);
+    const uint16_t plus = 0x3C00, minus = 0xBC00;   // fp16 +1, -1
+    for (int e = 0; e < 256; ++e)
+      for (int p = 0; p < 4; ++p)
+        sg[e * 4 + p] = pair(((e >> (2 * p)) & 1) ? plus : minus, ((e >> (2 * p + 1)) & 1) ? plus : minus);
   }
   {
     const int b = h.bits, mask = (1 << b) - 1;
@@ -419,6 +496,9 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
   a.qjl_rot_t = m > 0 ? dev_ptr<float>(kcb, kcb->off_qjl_rot_t_f32) : nullptr;
   a.k_lut = dev_ptr<float>(kcb, kcb->off_key_lut);
   a.k_pair = dev_ptr<float>(kcb, kcb->off_pair_lut);
+  a.mk_lut = dev_ptr<void>(kcb, kcb->off_mkey_lut);
+  a.sg_lut = dev_ptr<void>(kcb, kcb->off_sign_lut);
+  a.norm_vec4 = (k->t_cap % 4 == 0) && aligned(k->norms, 16) && (k->res_norms == nullptr || aligned(k->res_norms, 16));
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   a.ws_qslot = reinterpret_cast<float *>(ws + plan.off_qslot);
   a.ws_part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
@@ -459,6 +539,8 @@ tq_status prepare_decode(const tq_codebook *kcb, const tq_codebook *vcb, const v
   a.out_bf16 = (out_dtype == TQ_BF16);
   a.rot_v = dev_ptr<float>(vcb, vcb->off_rot_f32);
   a.v_lut = dev_ptr<float>(vcb, vcb->off_pair_lut);
+  a.mv_lut = dev_ptr<void>(vcb, vcb->off_mval_lut);
+  a.norm_vec4 = a.norm_vec4 && aligned(v->norms, 16);
   *out_args = a;
   return ok();
 }

@@ -53,5 +53,8 @@ struct tq_codebook {
   size_t off_key_lut = 0;         // decode key dequantization table
   size_t off_pair_lut = 0;        // decode value pair table
   size_t off_qcells = 0;          // encode quantizer cell table
+  size_t off_mkey_lut = 0;        // matrix-core decode: key operand table
+  size_t off_mval_lut = 0;        // matrix-core decode: value operand table
+  size_t off_sign_lut = 0;        // matrix-core decode: sign table
   float qscale = 0.f, qbias = 0.f;
 };

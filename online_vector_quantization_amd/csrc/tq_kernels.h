@@ -76,6 +76,17 @@ constexpr size_t kKeyLutBytes = 256 * 4 * sizeof(float);     // largest key tabl
 // Value pair table: 2^(2b) entries of (centroid[e & m], centroid[(e >> b) & m]).
 constexpr size_t kPairLutBytes = 256 * 2 * sizeof(float);
 
+// Operand tables of the matrix-core decode (built once per codebook on the
+// host).  Every centroid c is carried as one 32-bit word: its hi part in the
+// low half, lo = c - hi in the high half.  Key table: index (code a) | (code
+// b) << b', two words: the fp16 parts of 256 c_a, then of 256 c_b.  Value
+// table: index (code of token t) | (code of token t') << b', two words: the
+// bf16 parts of c_t, then of c_t'.  Sign table: a byte of sign bits -> eight
+// fp16 +-1 (set bit +1) in four words.
+constexpr size_t kMKeyLutBytes = 256 * 2 * sizeof(uint32_t);   // largest (b' = 4)
+constexpr size_t kMValLutBytes = 256 * 2 * sizeof(uint32_t);
+constexpr size_t kSignLutBytes = 256 * 4 * sizeof(uint32_t);
+
 struct DecodePlan {
   int chunk;               // tokens per work-group chunk
   int n_chunks;
@@ -124,6 +135,10 @@ struct DecodeArgs {
   const float *k_lut;      // key dequantization table (kKeyLutBytes)
   const float *v_lut;      // value pair table (kPairLutBytes)
   const float *k_pair;     // key pair table (kPairLutBytes layout, key codebook)
+  const void *mk_lut;          // key operand table of the key codebook
+  const void *mv_lut;          // value operand table of the value codebook
+  const void *sg_lut;          // sign table
+  int norm_vec4;               // t_cap % 4 == 0 and the norm arrays 16-byte aligned (four norms per load)
   float *ws_qslot;
   float *ws_part_o;        // [B*Hkv][n_chunks][g][d]: rotated back (decode kernel) or rotated (chunk kernel)
   float *ws_part_ml;       // [B*Hkv][n_chunks][g][2]
@@ -132,6 +147,19 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// The matrix-core decode's main launch (n_new = 1): the output for one-chunk
+// rows, else the chunks' partials for the merge launch; scores only with
+// scores_only (every l_t to a.scores, nothing else).
+hipError_t launch_mdecode_main(const DecodeArgs &a, bool scores_only, hipStream_t stream);
+// Rows up to this many tokens take the matrix-core decode (its per-lane cache
+// offsets are 32-bit byte offsets within a row: 72 bytes per token at most).
+constexpr int64_t kMDecodeMaxTcap = (int64_t{1} << 31) / 72;
+// Single-query decodes over rows of a multiple of 4 tokens (up to
+// kMDecodeMaxTcap) with 16-byte aligned norm arrays take the matrix-core
+// decode; others take the per-head vector decode.
+inline bool mdecode_applies(const DecodeArgs &a) {
+  return a.n_new == 1 && a.t_cap <= kMDecodeMaxTcap && a.norm_vec4 != 0;
+}
 // Scores only: the decode's key phase, writing every l_t to a.scores (no value
 // phase, no combine; the value fields are not read).
 hipError_t launch_logits(const DecodeArgs &a, hipStream_t stream);

@@ -1,0 +1,714 @@
+// Decode attention over the compressed KV cache on the matrix cores (gfx950,
+// v_mfma_f32_16x16x32_bf16): the g query heads of one KV head share every
+// dequantized key and value, so the per-token work is a dense (g heads x
+// tokens) contraction for the scores and a dense (g heads x tokens) x
+// (tokens x d) one for the value sum.  Dequantizing once per token row and
+// letting the matrix cores multiply removes the g-fold vector-ALU work of a
+// per-head decode.
+//
+// The arithmetic is the method's ([cc-newplayer explainer, technical
+// breakdown items 2 and 4]: the query is rotated once and stays uncompressed,
+// attention runs on the compressed K and V with dequantization;
+// [admirer.cn memory-wall article, section 2, stage two] and
+// [intelliparadigm "3-bit" article, §2.1.2]: the 1-bit QJL estimate of the
+// residual's inner product):
+//     l_t = scale * nu_t * ( <q~, c_k[code_t]> + sqrt(pi/2)/m * gamma_t * <s, 2 z_t - 1> ),
+//     o~  = sum_t softmax(l)_t nu^v_t c_v[code^v_t],   o = Pi_v^T o~,
+// with q~ = Pi_k q and s = S Pi_k q.
+//
+// fp32-level accuracy from 16-bit operands: every fp32 operand is split as
+// hi + lo.  The 16 columns of each product carry the g <= 8 heads twice:
+// column h holds the query's hi part and column 8 + h its lo part (for the
+// value sum: the weights' hi and lo parts), and the dequantized operand is
+// applied as its hi part and then its lo part.  The two columns of a head add
+// up to the full product (the +-1 signs are exact and need no lo part).  The
+// score products take fp16 parts (22 significant bits; per-head power-of-two
+// scales keep them in range), because a score can be a small difference of
+// large terms; the value sum, whose result only needs absolute accuracy,
+// takes bf16 parts.
+//
+// Work-group = (batch b, kv head, chunk of tokens), 8 waves.  Prologue:
+// q~ and s for the g heads in fp32 (partial dot products reduced in LDS), the
+// query operands split into registers, and three lookup tables in LDS (key
+// codes -> (hi, lo) centroid pairs, sign bytes -> eight +-1, pairs of tokens'
+// value codes -> (hi, lo) centroid pairs).  Main loop: each wave owns every
+// eighth 32-token tile of the chunk, with its own running max, sum and output
+// accumulators, and the next tile's records loaded into registers during the
+// current one.  Per tile and 16-token half: 8 MFMAs give the key term, 4 the
+// sign term; the score's two columns are added across lanes, the online
+// softmax (running max raised lazily) forms p nu^v, split hi/lo into the
+// value product's B operand; 16 MFMAs accumulate the value sum.  Epilogue:
+// the waves merge, Pi_v^T rotates the chunk's sum back, and the work-group
+// writes the output (one chunk per row) or its partial for the merge launch.
+//
+// Register layout of v_mfma_f32_16x16x32_bf16 (lane l, n = l % 16,
+// kq = l / 16): A operand A[n][8 kq .. 8 kq + 7]; B operand B[8 kq ..][n];
+// result C[4 kq + e][n], e = 0..3.  Here:
+//   scores  C[token][column] = K^(tokens x coords) Q(coords x columns): lane
+//           (n, kq) dequantizes token n's coordinates 32 kq + 8 s .. + 7 at
+//           k-step s (its KB code words in one load) and receives tokens
+//           4 kq + e of every column n;
+//   values  C[coord][column] = V^T(coords x tokens) P(tokens x columns): row n
+//           of block cb is coordinate 8 n + cb, so lane (n, kq) dequantizes
+//           coordinates 8 n .. 8 n + 7 (one 8 b'-bit field per token) of the
+//           tokens whose scores it received: the softmax output feeds the B
+//           operand without a transposition.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "tq_kernels.h"
+
+namespace tq {
+namespace {
+
+constexpr int D = kHeadDim;
+#ifndef TQ_MDEC_WAVES
+#define TQ_MDEC_WAVES 8
+#endif
+constexpr int kWaves = TQ_MDEC_WAVES;     // 8 or more (the prologue and epilogue use the first 512 threads)
+constexpr int kThreads = 64 * kWaves;
+static_assert(kWaves >= 8, "the prologue and the inverse rotation map 512 threads");
+constexpr int kTile = 32;                 // tokens per wave tile (two 16-token halves)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// A head's running max (log2 units) is raised only when a score exceeds it by
+// more than this, so the weights stay below 2^12 and most tiles rescale nothing.
+constexpr float kLazy2 = 12.f;
+// The key operand table holds fp16 hi/lo parts of 256 c (exact power-of-two
+// scale), which keeps every centroid's lo part in fp16's normal range.
+constexpr float kKeyScale = 256.f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  return __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
+}
+
+// (a, b) rounded to bf16 (nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  return __builtin_bit_cast(f16x8, make_uint4(w0, w1, w2, w3));
+}
+
+// The fp16 hi parts of (a, b) packed (a in the low half), or with lo set
+// their lo parts fp16(a - hi).  Both halves are exact in fp32, so hi + lo
+// carries 22 significant bits.
+__device__ __forceinline__ uint32_t split_f16(float a, float b, bool lo) {
+  const f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
+  const f16x2 l = __builtin_convertvector((f32x2){a - static_cast<float>(h[0]), b - static_cast<float>(h[1])}, f16x2);
+  return __builtin_bit_cast(uint32_t, lo ? l : h);
+}
+
+// The value of lane l ^ 8 (the other column of the same head): a rotation by
+// 8 within each row of 16 lanes.
+__device__ __forceinline__ float swap8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t swap8u(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float load_query(const void *q, int q_bf16, int64_t idx) {
+  if (q_bf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(q)[idx]) << 16);
+  return static_cast<const float *>(q)[idx];
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Striped LDS tables: entry e of copy j sits at byte e * kRow + j * kEntryBytes,
+// and lane (n, kq) reads copy n % kCopies.  The lanes that the LDS serves
+// together then read distinct banks whatever entries they pick.
+template <int ENTRY_BYTES, int COPIES> struct Striped {
+  static constexpr int kEntryBytes = ENTRY_BYTES;
+  static constexpr int kCopies = COPIES;
+  static constexpr int kRow = ENTRY_BYTES * COPIES;
+  static constexpr int kShift = __builtin_ctz(kRow);
+};
+constexpr int kPairCopies = 16;   // 8-byte entries: 16 lanes x 2 banks per pass
+constexpr int kSignCopies = 8;    // 16-byte entries: 8 lanes x 4 banks per pass
+using PairTab = Striped<8, kPairCopies>;
+using SignTab = Striped<16, kSignCopies>;
+
+// One wave's share of a 32-token tile: its records, loaded one tile ahead.
+template <int KB, int VB, bool QJL, bool SC> struct Tile {
+  uint32_t kc[2][KB];          // key code words kq KB .. of token n of each half
+  uint32_t sg[2];              // sign word kq of token n of each half
+  float knu[4], gam[4];        // tokens 4 kq + e of the lane's own half (columns 0..7: the first)
+  uint32_t vf[SC ? 1 : 8][VB == 3 ? 2 : 1];   // value words holding coordinates 8 n .. 8 n + 7 of tokens T(i)
+  float vnu[SC ? 1 : 4];       // value norms of the lane's own half's tokens
+};
+
+// Token T(i) of the lane's value fields: 4 kq + (i & 3) of half i >> 2.
+// One code path for every tile (the compiler's wait counts then stay exact
+// across iterations): token indices are clamped to the row's last cached
+// token (tiles past seq_len are masked when used), byte offsets are 32-bit
+// on a uniform row base, and the norms come four at a time (the row length
+// is a multiple of 4 and the norm arrays 16-byte aligned on this path).
+template <int KB, int VB, bool QJL, bool SC>
+__device__ __forceinline__ void load_tile(const DecodeArgs &a, int64_t row0, int tb, int n, int kq, bool lo_col,
+                                          Tile<KB, VB, QJL, SC> &r) {
+  constexpr int VW = 4 * VB;
+  const int last = static_cast<int>(a.t_cap) - 1;
+  const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k_codes + row0 * (4 * KB));
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const uint32_t tk = static_cast<uint32_t>(min(tb + 16 * hf + n, last));
+    const uint32_t ko = (tk * (4 * KB) + kq * KB) * 4u;
+#pragma unroll
+    for (int w = 0; w < KB; ++w) r.kc[hf][w] = *reinterpret_cast<const uint32_t *>(kbase + 4 * w + ko);
+    if constexpr (QJL)
+      r.sg[hf] = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const unsigned char *>(a.k_signs + row0 * 4) +
+                                                     (tk * 4u + kq) * 4u);
+  }
+  // four consecutive tokens 4 kq .. 4 kq + 3 of the lane's own half (aligned
+  // to 4; a group past the row's end repeats its last group, masked later)
+  const uint32_t t4 = static_cast<uint32_t>(min(tb + 16 * (lo_col ? 1 : 0) + 4 * kq, last - 3)) * 4u;
+  const float4 nv = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(a.k_norms + row0) + t4);
+  r.knu[0] = nv.x; r.knu[1] = nv.y; r.knu[2] = nv.z; r.knu[3] = nv.w;
+  if constexpr (QJL) {
+    const float4 gv = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(a.k_res + row0) + t4);
+    r.gam[0] = gv.x; r.gam[1] = gv.y; r.gam[2] = gv.z; r.gam[3] = gv.w;
+  }
+  if constexpr (!SC) {
+    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v_codes + row0 * VW);
+    const int w0 = (8 * n * VB) >> 5;   // first word of the lane's value field
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t tv = static_cast<uint32_t>(min(tb + 16 * (i >> 2) + 4 * kq + (i & 3), last));
+      const uint32_t vo = (tv * VW + w0) * 4u;
+      r.vf[i][0] = *reinterpret_cast<const uint32_t *>(vbase + vo);
+      if constexpr (VB == 3) r.vf[i][1] = (w0 + 1 < VW) ? *reinterpret_cast<const uint32_t *>(vbase + vo + 4) : 0u;
+    }
+    const float4 vv = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(a.v_norms + row0) + t4);
+    r.vnu[0] = vv.x; r.vnu[1] = vv.y; r.vnu[2] = vv.z; r.vnu[3] = vv.w;
+  }
+}
+
+// The 8 b'-bit field of coordinates 8 n .. 8 n + 7 of one token.
+template <int VB>
+__device__ __forceinline__ uint32_t value_field(const uint32_t (&w)[VB == 3 ? 2 : 1], int n) {
+  const int sh = (8 * n * VB) & 31;
+  if constexpr (VB == 4) return w[0];
+  if constexpr (VB == 3) return __builtin_amdgcn_alignbit(w[1], w[0], sh) & 0xFFFFFFu;
+  if constexpr (VB == 2) return (w[0] >> sh) & 0xFFFFu;
+  return (w[0] >> sh) & 0xFFu;
+}
+
+// Even-indexed codes of an 8-code field (VB bits each), kept in place.
+template <int VB> struct EvenMask;
+template <> struct EvenMask<1> { static constexpr uint32_t v = 0x55u; };
+template <> struct EvenMask<2> { static constexpr uint32_t v = 0x3333u; };
+template <> struct EvenMask<3> { static constexpr uint32_t v = 0x1C71C7u; };
+template <> struct EvenMask<4> { static constexpr uint32_t v = 0x0F0F0F0Fu; };
+
+template <int KB, int VB, bool QJL, bool SC>
+__global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
+  constexpr int kKeyEntries = 1 << (2 * KB);
+  constexpr int kValEntries = SC ? 1 : 1 << (2 * VB);
+  struct Smem {
+    alignas(16) unsigned char ktab[kKeyEntries * PairTab::kRow];
+    alignas(16) unsigned char vtab[kValEntries * PairTab::kRow];
+    alignas(16) unsigned char stab[QJL ? 256 * SignTab::kRow : 16];
+    union {
+      struct {
+        float q[8][D];                 // the g queries
+        float part[4][8][D];           // partial dot products of q~
+        float part_s[QJL ? 4 : 1][8][D];   // and of s
+        float qt[8][D];                // q~ (scaled), [head][coordinate]
+        float st[8][D];                // s (scaled)
+        int fexp[8][2];                // per head: the fp16 operands' power-of-two scales
+      } pro;
+      struct {
+        // each wave's rotated sum, weighted by its max: coordinate c of head h
+        // at [c / 32][h][c % 32] (rows of 33 words: the 32 lanes that store
+        // one register, (h, c / 32) = (lane % 8, lane / 16), hit 32 banks)
+        float o[kWaves][4][8][33];
+      } epi;
+      struct {
+        float ot[8][D];          // the work-group's rotated sum
+        float red[4][8][D];      // quarter products of Pi_v^T
+      } inv;
+    } u;
+    float ml[kWaves][8][2];
+  };
+  __shared__ Smem sm;
+
+  const int chunk_id = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kq = lane >> 4;
+  const bool lo_col = n >= 8;
+  const int hcol = n & 7;                  // the head of this lane's column
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const bool live_col = hcol < G;
+  const int row_id = b * a.n_kv_heads + hk;
+  const int group_id = row_id * a.n_chunks + chunk_id;
+  const int64_t row0 = static_cast<int64_t>(row_id) * a.t_cap;
+  int T = a.seq_len[b] + a.seq_add;
+  T = T < 0 ? 0 : (T > a.t_cap ? static_cast<int>(a.t_cap) : T);
+  const int t_begin = chunk_id * a.chunk;
+  const int t_end = min(T, t_begin + a.chunk);
+
+  // The wave's first tile is requested before the prologue, whose work then
+  // hides its memory latency.
+  Tile<KB, VB, QJL, SC> ta{};
+  int t0 = t_begin + wave * kTile;
+  if (t0 < t_end) load_tile<KB, VB, QJL, SC>(a, row0, t0, n, kq, lo_col, ta);
+
+  // ------------------------------------------------------------ prologue
+  // Striped copies of the codebooks' tables (key code pairs -> fp16 (hi, lo)
+  // of 256 c per code, pairs of tokens' value codes -> bf16 (hi, lo) of c per
+  // token, sign bytes -> eight fp16 +-1).
+  {
+    const uint2 *kt = reinterpret_cast<const uint2 *>(a.mk_lut);
+    for (int i = tid; i < kKeyEntries * PairTab::kCopies; i += kThreads)
+      *reinterpret_cast<uint2 *>(sm.ktab + (i / PairTab::kCopies) * PairTab::kRow + (i % PairTab::kCopies) * 8) =
+          kt[i / PairTab::kCopies];
+    if constexpr (!SC) {
+      const uint2 *vt = reinterpret_cast<const uint2 *>(a.mv_lut);
+      for (int i = tid; i < kValEntries * PairTab::kCopies; i += kThreads)
+        *reinterpret_cast<uint2 *>(sm.vtab + (i / PairTab::kCopies) * PairTab::kRow + (i % PairTab::kCopies) * 8) =
+            vt[i / PairTab::kCopies];
+    }
+    if constexpr (QJL) {
+      const uint4 *st = reinterpret_cast<const uint4 *>(a.sg_lut);
+      for (int i = tid; i < 256 * SignTab::kCopies; i += kThreads)
+        *reinterpret_cast<uint4 *>(sm.stab + (i / SignTab::kCopies) * SignTab::kRow + (i % SignTab::kCopies) * 16) =
+            st[i / SignTab::kCopies];
+    }
+  }
+  // q~ = Pi_k q and s = (S Pi_k) q of the g heads in fp32: thread (i, part)
+  // forms the partial dot products over input coordinates 32 part .. + 31 of
+  // column i of Pi_k^T and of (S Pi_k)^T (every global read issued first),
+  // summed over the four parts in LDS.
+  {
+    const int pi_ = tid & (D - 1), part = tid >> 7;
+    const bool in_pro = part < 4;   // wave-uniform: the first 512 threads
+    float pv[32], sv[QJL ? 32 : 1];
+    if (in_pro) {
+#pragma unroll
+      for (int jj = 0; jj < 32; ++jj) pv[jj] = a.rot_k_t[(32 * part + jj) * D + pi_];
+      if constexpr (QJL) {
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) sv[jj] = a.qjl_rot_t[(32 * part + jj) * kQjlDim + pi_];
+      }
+    }
+    for (int e = tid; e < 8 * D; e += kThreads)
+      sm.u.pro.q[e / D][e % D] =
+          (e / D < G) ? load_query(a.q, a.q_bf16, (static_cast<int64_t>(b) * a.n_q_heads + hk * G + e / D) * D + e % D)
+                      : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      if (in_pro && h < G) {
+        float aq = 0.f, as = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) {
+          const float qj = sm.u.pro.q[h][32 * part + jj];
+          aq = fmaf(pv[jj], qj, aq);
+          if constexpr (QJL) as = fmaf(sv[jj], qj, as);
+        }
+        sm.u.pro.part[part][h][pi_] = aq;
+        if constexpr (QJL) sm.u.pro.part_s[part][h][pi_] = as;
+      }
+    }
+    __syncthreads();
+    // scaled by scale * log2 e (the sign term also by sqrt(pi/2)/m); heads past g are zero
+    const float qsc = a.scale * kLog2e, ssc = a.scale * kLog2e * a.qjl_coef;
+    for (int e = tid; e < 8 * D; e += kThreads) {
+      const int h = e / D, i = e % D;
+      float v = 0.f, w = 0.f;
+      if (h < G) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          v += sm.u.pro.part[pp][h][i];
+          if constexpr (QJL) w += sm.u.pro.part_s[pp][h][i];
+        }
+      }
+      sm.u.pro.qt[h][i] = v * qsc;
+      sm.u.pro.st[h][i] = w * ssc;
+    }
+    __syncthreads();
+    // per head, a power of two that brings the largest |q~| (and |s|) into
+    // [64, 128): the fp16 operands then keep full precision and cannot overflow
+    if (wave < 8) {
+      const int h = wave;   // one wave per head slot
+      float mq = fmaxf(fabsf(sm.u.pro.qt[h][lane]), fabsf(sm.u.pro.qt[h][lane + 64]));
+      float ms = fmaxf(fabsf(sm.u.pro.st[h][lane]), fabsf(sm.u.pro.st[h][lane + 64]));
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        mq = fmaxf(mq, __shfl_xor(mq, off));
+        ms = fmaxf(ms, __shfl_xor(ms, off));
+      }
+      if (lane == 0) {
+        int eq = 0, es = 0;
+        (void)frexpf(mq, &eq);
+        (void)frexpf(ms, &es);
+        sm.u.pro.fexp[h][0] = (mq > 0.f && mq < INFINITY) ? 7 - eq : 0;
+        sm.u.pro.fexp[h][1] = (ms > 0.f && ms < INFINITY) ? 7 - es : 0;
+      }
+    }
+  }
+  __syncthreads();
+  // The scores' B operands, column n: the query part of head n % 8 times
+  // 2^fexp (fp16 hi part in columns 0..7, lo part in 8..15, zero for columns
+  // past g).  Key product, k-step s: K-element pair i carries coordinate
+  // 32 kq + 4 s + i twice (the key operand holds its (hi, lo) parts); sign
+  // product, k-step s: coordinates 32 kq + 8 s .. + 7 once.  The products
+  // come out scaled by 2^fexp_q * kKeyScale (key term) and 2^fexp_s (sign
+  // term): undone per lane below.
+  f16x8 qop[8], sop[QJL ? 4 : 1];
+  const int eq = sm.u.pro.fexp[hcol][0], es = sm.u.pro.fexp[hcol][1];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    uint32_t wq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = ldexpf(sm.u.pro.qt[hcol][32 * kq + 4 * s + i], eq);
+      wq[i] = split_f16(x, x, lo_col);
+    }
+    qop[s] = as_f16x8(wq[0], wq[1], wq[2], wq[3]);
+  }
+  if constexpr (QJL) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t ws[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int c = 32 * kq + 8 * s + 2 * p;
+        ws[p] = split_f16(ldexpf(sm.u.pro.st[hcol][c], es), ldexpf(sm.u.pro.st[hcol][c + 1], es), lo_col);
+      }
+      sop[s] = as_f16x8(ws[0], ws[1], ws[2], ws[3]);
+    }
+  }
+  // l2 = nu * (key term + gamma * sign term) with the operand scales undone:
+  // key products carry 2^eq * kKeyScale, sign products 2^es
+  const float inv_k = ldexpf(1.f / kKeyScale, -eq);
+  const float rat_s = ldexpf(kKeyScale, eq - es);   // sign term in key-product units
+
+  // ------------------------------------------------------------ main loop
+  float m_run = -INFINITY;   // this head's running max (log2 units), equal in all its lanes
+  float l_lane = 0.f;        // sum of this lane's weights
+  f32x4 oacc[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t lane_p = 8u * (n % PairTab::kCopies);   // this lane's copy in the pair tables
+  const uint32_t lane_s = 16u * (n % SignTab::kCopies);  // and in the sign table
+
+  // One tile: scores (key and sign products), online softmax, value product.
+  auto compute = [&](const Tile<KB, VB, QJL, SC> &cur, int tb) {
+    const bool full = tb + kTile <= t_end;
+    // ---- scores C[token 4 kq + e][column n] of both halves.  K-element
+    // pair i of k-step s is (hi, lo) of coordinate 32 kq + 4 s + i (keys), or
+    // signs 32 kq + 8 s + 2 i, + 1 (sign term).
+    f32x4 sacc[2], tacc[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      sacc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tacc[hf] = sacc[hf];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        uint32_t ka[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          // pair q = 2 s + p: bits [2 KB q, 2 KB q + 2 KB) of the lane's codes
+          constexpr int kMask = (1 << (2 * KB)) - 1;
+          const int bit = 2 * KB * (2 * s + p), w = bit >> 5, sh = bit & 31;
+          uint32_t idx;
+          if (sh + 2 * KB <= 32) {
+            idx = (cur.kc[hf][w] >> sh) & kMask;
+          } else {
+            idx = __builtin_amdgcn_alignbit(cur.kc[hf][w + 1], cur.kc[hf][w], sh) & kMask;
+          }
+          ka[p] = (idx << PairTab::kShift) + lane_p;
+        }
+        const uint2 e0 = *reinterpret_cast<const uint2 *>(sm.ktab + ka[0]);
+        const uint2 e1 = *reinterpret_cast<const uint2 *>(sm.ktab + ka[1]);
+        sacc[hf] = mfma_f16(as_f16x8(e0.x, e0.y, e1.x, e1.y), qop[s], sacc[hf]);
+      }
+      if constexpr (QJL) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t by = (cur.sg[hf] >> (8 * s)) & 255u;
+          const uint4 z = *reinterpret_cast<const uint4 *>(sm.stab + (by << SignTab::kShift) + lane_s);
+          tacc[hf] = mfma_f16(as_f16x8(z.x, z.y, z.z, z.w), sop[s], tacc[hf]);
+        }
+      }
+    }
+    // ---- the head's full score: its two columns summed across lanes n and
+    // n ^ 8; lanes of columns 0..7 keep the first half's tokens, 8..15 the second's
+    const int tk0 = tb + 16 * (lo_col ? 1 : 0) + 4 * kq;
+    float l2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float y = (lo_col ? sacc[1][e] : sacc[0][e]) + swap8(lo_col ? sacc[0][e] : sacc[1][e]);
+      if constexpr (QJL) {
+        const float yt = (lo_col ? tacc[1][e] : tacc[0][e]) + swap8(lo_col ? tacc[0][e] : tacc[1][e]);
+        y = fmaf(cur.gam[e] * rat_s, yt, y);
+      }
+      l2[e] = (full || tk0 + e < t_end) ? (cur.knu[e] * inv_k) * y : -INFINITY;
+    }
+    if (SC || a.scores != nullptr) {
+      if (live_col) {
+        float *sp = a.scores + (static_cast<int64_t>(b) * a.n_q_heads + hk * G + hcol) * a.t_cap;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (full || tk0 + e < t_end) sp[tk0 + e] = l2[e] * kLn2;
+      }
+    }
+    if constexpr (!SC) {
+      // ---- online softmax, running max raised lazily (wave-uniform decision)
+      const float tmax = fmaxf(fmaxf(l2[0], l2[1]), fmaxf(l2[2], l2[3]));
+      if (__any(tmax > m_run + kLazy2)) {
+        float hm = fmaxf(tmax, swap8(tmax));
+        hm = fmaxf(hm, __shfl_xor(hm, 16));
+        hm = fmaxf(hm, __shfl_xor(hm, 32));
+        const float m_new = fmaxf(m_run, hm);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_lane *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) oacc[cb] *= alpha;
+      }
+      float w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = full || tk0 + e < t_end;
+        const float p = valid ? __builtin_amdgcn_exp2f(l2[e] - m_run) : 0.f;
+        l_lane += p;
+        w[e] = valid ? p * cur.vnu[e] : 0.f;
+      }
+      // B operands of the value products, one per half: K-element pair i =
+      // token 4 kq + i of that half, the weight's hi part (columns 0..7) or lo
+      // part (8..15) twice.  A lane holds its own half's weights; the other
+      // half's part comes from lane n ^ 8.
+      const uint32_t h01 = pack_bf16(w[0], w[1]), h23 = pack_bf16(w[2], w[3]);
+      const uint32_t l01 = pack_bf16(w[0] - __uint_as_float(h01 << 16), w[1] - __uint_as_float(h01 & 0xffff0000u));
+      const uint32_t l23 = pack_bf16(w[2] - __uint_as_float(h23 << 16), w[3] - __uint_as_float(h23 & 0xffff0000u));
+      const uint32_t own01 = lo_col ? l01 : h01, own23 = lo_col ? l23 : h23;
+      const uint32_t r01 = swap8u(lo_col ? h01 : l01), r23 = swap8u(lo_col ? h23 : l23);
+      bf16x8 pb[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const bool mine = (hf == 1) == lo_col;
+        const uint32_t p01 = mine ? own01 : r01, p23 = mine ? own23 : r23;
+        pb[hf] = as_bf16x8(__builtin_amdgcn_perm(p01, p01, 0x01000100u), __builtin_amdgcn_perm(p01, p01, 0x03020302u),
+                           __builtin_amdgcn_perm(p23, p23, 0x01000100u), __builtin_amdgcn_perm(p23, p23, 0x03020302u));
+      }
+      // ---- value sum: block cb, row n = coordinate 8 n + cb; K-element pair
+      // i = (hi, lo) of token 4 kq + i of the half
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint32_t E[2], O[2];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          // tokens (2 pp, 2 pp + 1) of the half: the pair index of every
+          // coordinate, even coordinates in E, odd ones in O
+          constexpr uint32_t M = EvenMask<VB>::v;
+          const uint32_t f0 = value_field<VB>(cur.vf[4 * hf + 2 * pp], n);
+          const uint32_t f1 = value_field<VB>(cur.vf[4 * hf + 2 * pp + 1], n);
+          E[pp] = (f0 & M) | ((f1 & M) << VB);
+          O[pp] = ((f0 >> VB) & M) | (f1 & (M << VB));
+        }
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+          constexpr uint32_t kMask = (1u << (2 * VB)) - 1u;
+          const int sh = 2 * VB * (cb >> 1);
+          const uint32_t i0 = (((cb & 1) ? O[0] : E[0]) >> sh) & kMask;
+          const uint32_t i1 = (((cb & 1) ? O[1] : E[1]) >> sh) & kMask;
+          const uint2 e0 = *reinterpret_cast<const uint2 *>(sm.vtab + (i0 << PairTab::kShift) + lane_p);
+          const uint2 e1 = *reinterpret_cast<const uint2 *>(sm.vtab + (i1 << PairTab::kShift) + lane_p);
+          oacc[cb] = mfma(as_bf16x8(e0.x, e0.y, e1.x, e1.y), pb[hf], oacc[cb]);
+        }
+      }
+    }
+  };
+
+  constexpr int kStride = kWaves * kTile;
+  Tile<KB, VB, QJL, SC> tn{};
+  // two tile buffers in turn: one is computed while the next is loaded
+  for (; t0 < t_end; t0 += 2 * kStride) {
+    if (t0 + kStride < t_end) load_tile<KB, VB, QJL, SC>(a, row0, t0 + kStride, n, kq, lo_col, tn);
+    compute(ta, t0);
+    if (t0 + kStride >= t_end) break;
+    if (t0 + 2 * kStride < t_end) load_tile<KB, VB, QJL, SC>(a, row0, t0 + 2 * kStride, n, kq, lo_col, ta);
+    compute(tn, t0 + kStride);
+  }
+
+  if constexpr (SC) return;   // uniform: no barrier follows for any thread
+
+  // ------------------------------------------------------------ merge waves
+  // Pi_v^T of the chunk's sum: thread (i4, q4) applies rows 32 q4 .. + 31 of
+  // column i4 of Pi_v; requested now so that the merge hides their latency.
+  const int i4 = tid & (D - 1), q4 = tid >> 7;
+  const bool in_inv = q4 < 4;   // wave-uniform: the first 512 threads
+  float pvr[32];
+  if (in_inv) {
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) pvr[jj] = a.rot_v[(32 * q4 + jj) * D + i4];
+  }
+  // the head's sum over its 8 lanes (columns n, n ^ 8 and the four kq)
+  float lh = l_lane + swap8(l_lane);
+  lh += __shfl_xor(lh, 16);
+  lh += __shfl_xor(lh, 32);
+  if (lane < 8) {
+    sm.ml[wave][lane][0] = m_run;
+    sm.ml[wave][lane][1] = lh;
+  }
+  __syncthreads();
+  {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.ml[w][hcol][0]);
+    const float fw = (m_run == -INFINITY) ? 0.f : exp2f(m_run - mx);
+    // rows 4 kq + e of block cb are coordinates 8 (4 kq + e) + cb
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = (oacc[cb][e] + swap8(oacc[cb][e])) * fw;
+        if (!lo_col) sm.u.epi.o[wave][kq][hcol][8 * e + cb] = v;   // coordinate 32 kq + 8 e + cb
+      }
+  }
+  __syncthreads();
+  {
+    constexpr int kPer = (8 * D + kThreads - 1) / kThreads;
+    float s[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = tid + k * kThreads;   // (head, coordinate)
+      float v = 0.f;
+      if (e < 8 * D) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v += sm.u.epi.o[w][(e % D) >> 5][e / D][e & 31];
+      }
+      s[k] = v;
+    }
+    __syncthreads();   // every wave's sums are read: the region is reused
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = tid + k * kThreads;
+      if (e < 8 * D) sm.u.inv.ot[e / D][e % D] = s[k];
+    }
+  }
+  __syncthreads();
+  if (in_inv) {
+    float r[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) r[h] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj)
+#pragma unroll
+      for (int h = 0; h < 8; ++h)
+        if (h < G) r[h] = fmaf(pvr[jj], sm.u.inv.ot[h][32 * q4 + jj], r[h]);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) sm.u.inv.red[q4][h][i4] = r[h];
+  }
+  __syncthreads();
+  // the chunk's (max, sum) per head, max in natural-log units (the merge's)
+  auto chunk_ml = [&](int h, float &mx, float &lsum) {
+    mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.ml[w][h][0]);
+    lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (sm.ml[w][h][0] != -INFINITY) lsum += sm.ml[w][h][1] * exp2f(sm.ml[w][h][0] - mx);
+  };
+  if (a.n_chunks == 1 && a.seq_inc == nullptr) {
+    for (int e = tid; e < G * D; e += kThreads) {
+      const int h = e / D, i = e % D;
+      float mx, lsum;
+      chunk_ml(h, mx, lsum);
+      const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+      const float o = fmaf(inv, sm.u.inv.red[0][h][i] + sm.u.inv.red[1][h][i] + sm.u.inv.red[2][h][i] +
+                                    sm.u.inv.red[3][h][i], 0.f);
+      const int64_t o_idx = (static_cast<int64_t>(b) * a.n_q_heads + hk * G + h) * D + i;
+      if (a.out_bf16) {
+        static_cast<uint16_t *>(a.out)[o_idx] = f32_to_bf16_rne(o);
+      } else {
+        static_cast<float *>(a.out)[o_idx] = o;
+      }
+    }
+    return;
+  }
+  float *part_o = a.ws_part_o + static_cast<int64_t>(group_id) * G * D;
+  for (int e = tid; e < G * D; e += kThreads) {
+    const int h = e / D, i = e % D;
+    part_o[e] = sm.u.inv.red[0][h][i] + sm.u.inv.red[1][h][i] + sm.u.inv.red[2][h][i] + sm.u.inv.red[3][h][i];
+  }
+  if (tid < G) {
+    float mx, lsum;
+    chunk_ml(tid, mx, lsum);
+    a.ws_part_ml[(static_cast<int64_t>(group_id) * G + tid) * 2 + 0] = mx * kLn2;
+    a.ws_part_ml[(static_cast<int64_t>(group_id) * G + tid) * 2 + 1] = lsum;
+  }
+}
+
+template <int KB, bool QJL, bool SC>
+hipError_t launch_v(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+  if constexpr (SC) {
+    // scores only: no value table (the VB argument is unused)
+    hipLaunchKernelGGL((mdecode_kernel<KB, 4, QJL, true>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    switch (a.v_bits) {
+#define TQ_V(VV) \
+  case VV: hipLaunchKernelGGL((mdecode_kernel<KB, VV, QJL, false>), grid, dim3(kThreads), 0, stream, a); break;
+      TQ_V(1) TQ_V(2) TQ_V(3) TQ_V(4)
+#undef TQ_V
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int KB, bool SC>
+hipError_t launch_k(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+  return a.qjl_m > 0 ? launch_v<KB, true, SC>(a, grid, stream) : launch_v<KB, false, SC>(a, grid, stream);
+}
+
+}  // namespace
+
+hipError_t launch_mdecode_main(const DecodeArgs &a, bool scores_only, hipStream_t stream) {
+  const int g = a.n_q_heads / a.n_kv_heads;
+  if (!mdecode_applies(a) || a.n_chunks > kMaxDecodeChunks || g < 1 || g > 8 || a.n_kv_heads > 65535 ||
+      a.mk_lut == nullptr || a.rot_k_t == nullptr || (a.qjl_m > 0 && (a.qjl_rot_t == nullptr || a.sg_lut == nullptr)) ||
+      (!scores_only && a.mv_lut == nullptr))
+    return hipErrorInvalidValue;
+  const dim3 grid(a.n_chunks, a.n_kv_heads, a.batch);
+  switch (a.k_bits) {
+    case 1: return scores_only ? launch_k<1, true>(a, grid, stream) : launch_k<1, false>(a, grid, stream);
+    case 2: return scores_only ? launch_k<2, true>(a, grid, stream) : launch_k<2, false>(a, grid, stream);
+    case 3: return scores_only ? launch_k<3, true>(a, grid, stream) : launch_k<3, false>(a, grid, stream);
+    case 4: return scores_only ? launch_k<4, true>(a, grid, stream) : launch_k<4, false>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tq
