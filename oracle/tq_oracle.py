@@ -354,7 +354,9 @@ def decode_attention(q, kcache, vcache, seq_len, kbook, vbook, scale=None, retur
 
     q[B, Hq, d].  kcache: dict(codes[B,Hkv,Tcap,Wk] u32, signs[B,Hkv,Tcap,Ws] u32
     or None, norms[B,Hkv,Tcap], res_norms or None).  vcache: dict(codes, norms).
-    kbook/vbook: dict(bits, centroids, Pi, S (keys, or None)).
+    kbook/vbook: dict(bits, centroids, Pi, S (keys, or None)); a split-width
+    book (section 8) has n_wide > 0 and the wide / narrow codebooks instead of
+    centroids, and its records are read with book_codes / book_table.
     q-head h reads KV head h // (Hq/Hkv).  Scale defaults to 1/sqrt(d).  No
     mask: the decode query sees all seq_len[b] cached tokens.  An empty cache
     (seq_len 0) gives a zero output.  Steps: scores (decode_scores), softmax,
@@ -377,14 +379,14 @@ def decode_attention(q, kcache, vcache, seq_len, kbook, vbook, scale=None, retur
         for hk in range(Hkv):
             if T == 0:
                 continue
-            k_idx = unpack_bits(kcache["codes"][b, hk, :T], d, kbook["bits"])
+            k_idx = book_codes(kbook, kcache["codes"][b, hk, :T], d)
             k_z = unpack_bits(kcache["signs"][b, hk, :T], m, 1).astype(bool) if m else None
             k_gamma = kcache["res_norms"][b, hk, :T] if m else None
-            v_idx = unpack_bits(vcache["codes"][b, hk, :T], d, vbook["bits"])
-            vdeq = dequant_values(vbook["Pi"], vbook["centroids"], v_idx, vcache["norms"][b, hk, :T])
+            v_idx = book_codes(vbook, vcache["codes"][b, hk, :T], d)
+            vdeq = dequant_values(vbook["Pi"], book_table(vbook), v_idx, vcache["norms"][b, hk, :T])
             for j in range(g):
                 h = hk * g + j
-                l = decode_scores(q[b, h], kbook["Pi"], kbook["centroids"], kbook.get("S"),
+                l = decode_scores(q[b, h], kbook["Pi"], book_table(kbook), kbook.get("S"),
                                   k_idx, kcache["norms"][b, hk, :T], k_gamma, k_z, scale)
                 scores[b, h, :T] = l
                 out[b, h] = softmax(l) @ vdeq
@@ -423,3 +425,147 @@ def exact_attention(q, k, v, scale=None):
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     return softmax(scale * (k @ q)) @ v
+
+
+# --------------------------------------------------------------------------
+# 8. Split bit widths  [explainer §1], [3-bit §2.1], [3-bit §5.1]
+# --------------------------------------------------------------------------
+# The pages quote fractional average widths (about 2.5 bits per element in the
+# explainer's asymmetric mixed-precision item, a "2.5-bit" intermediate in the
+# 3-bit article's pipeline figure, 3.5 bits in its limits section) without
+# saying how a fraction is reached.  Reading: a fixed split of the d rotated
+# coordinates -- the first n_wide get the (b+1)-bit Lloyd-Max codebook, the
+# other d - n_wide the b-bit one -- for b + n_wide/d bits per coordinate (keys
+# add their 1-bit sketch on top).  Every rotated coordinate follows the same
+# law f_d, so each width's codebook is the uniform case's, and which
+# coordinates are wide does not change the expected distortion.  Storage: code
+# j starts at bit offset sum_{i<j} width_i of the vector's stream (the uniform
+# layout of section 6 when every width is equal).
+
+
+def split_widths(d: int, bits: int, n_wide: int) -> np.ndarray:
+    """Per-coordinate widths: bits + 1 for j < n_wide, bits for the rest."""
+    if not 0 <= n_wide <= d:
+        raise ValueError("n_wide must lie in [0, d]")
+    w = np.full(d, bits, dtype=np.int64)
+    w[:n_wide] = bits + 1
+    return w
+
+
+def build_split_book(d: int, bits: int, n_wide: int) -> dict:
+    """The two stored codebooks of a split: fp32 (centroids, thresholds) of
+    widths bits + 1 ("wide") and bits ("narrow"), and the split point."""
+    return {"bits": bits, "n_wide": n_wide, "wide": build_codebook(d, bits + 1), "narrow": build_codebook(d, bits)}
+
+
+def quantize_split(y, split: dict) -> np.ndarray:
+    """Each coordinate's code from its own width's thresholds (quantize())."""
+    y = np.asarray(y)
+    nw = split["n_wide"]
+    idx = np.empty(y.shape, dtype=np.int64)
+    idx[..., :nw] = quantize(y[..., :nw], split["wide"][1])
+    idx[..., nw:] = quantize(y[..., nw:], split["narrow"][1])
+    return idx
+
+
+def dequant_split(idx, split: dict) -> np.ndarray:
+    """Rotated reconstruction: coordinate j is its width's centroid c[idx_j]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    nw = split["n_wide"]
+    out = np.empty(idx.shape, dtype=np.float64)
+    out[..., :nw] = np.asarray(split["wide"][0], dtype=np.float64)[idx[..., :nw]]
+    out[..., nw:] = np.asarray(split["narrow"][0], dtype=np.float64)[idx[..., nw:]]
+    return out
+
+
+def encode_split(x, Pi, split: dict, S=None):
+    """encode() with per-coordinate widths: the same stages, each rotated
+    coordinate quantized by its own width's codebook; the residual (keys) is
+    y minus that reconstruction."""
+    x = np.asarray(x, dtype=np.float64)
+    nu = np.sqrt(np.sum(x * x, axis=1))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        inv = np.where(nu == 0.0, 0.0, 1.0 / nu)
+    y = (x * inv[:, None]) @ np.asarray(Pi, dtype=np.float64).T
+    idx = quantize_split(y, split)
+    out = {"nu": nu, "y": y, "idx": idx}
+    if S is not None:
+        r = y - dequant_split(idx, split)
+        gamma = np.sqrt(np.sum(r * r, axis=1))
+        p = r @ np.asarray(S, dtype=np.float64).T
+        out.update(r=r, gamma=gamma, p=p, z=(p > 0))
+    return out
+
+
+def coord_mse(d: int, centroids, thresholds) -> float:
+    """E[(Y - c(Y))^2] for one coordinate Y ~ f_d under the quantizer (c, t)."""
+    c = np.asarray(centroids, dtype=np.float64)
+    edges = np.concatenate(([-1.0], np.asarray(thresholds, dtype=np.float64), [1.0]))
+    mass = np.diff(coord_cdf(edges, d))
+    moment = np.diff(coord_partial_mean(edges, d))
+    return 1.0 / d - 2.0 * np.sum(c * moment) + np.sum(c * c * mass)
+
+
+def split_distortion(d: int, split: dict) -> float:
+    """E||u - u_hat||^2 of a unit vector under a split: the sum over the d
+    rotated coordinates of each one's MSE under its own width's codebook."""
+    nw = split["n_wide"]
+    total = 0.0
+    for j in range(d):
+        c, t = split["wide"] if j < nw else split["narrow"]
+        total += coord_mse(d, c, t)
+    return total
+
+
+def pack_bits_widths(vals, widths) -> np.ndarray:
+    """Pack codes vals[n, d] with per-coordinate widths into uint32 words
+    [n, ceil(sum(widths)/32)]: code j at bit offset sum_{i<j} widths_i."""
+    vals = np.asarray(vals, dtype=np.int64)
+    widths = np.asarray(widths, dtype=np.int64)
+    n, d = vals.shape
+    words = np.zeros((n, (int(widths.sum()) + 31) // 32), dtype=np.uint64)
+    k = 0
+    for j in range(d):
+        for b in range(int(widths[j])):
+            bit = ((vals[:, j] >> b) & 1).astype(np.uint64)
+            words[:, k // 32] |= bit << np.uint64(k % 32)
+            k += 1
+    return words.astype(np.uint32)
+
+
+def unpack_bits_widths(words, widths) -> np.ndarray:
+    """Inverse of pack_bits_widths."""
+    words = np.asarray(words, dtype=np.uint32).astype(np.uint64)
+    widths = np.asarray(widths, dtype=np.int64)
+    n = words.shape[0]
+    vals = np.zeros((n, widths.size), dtype=np.int64)
+    k = 0
+    for j in range(widths.size):
+        for b in range(int(widths[j])):
+            bit = (words[:, k // 32] >> np.uint64(k % 32)) & np.uint64(1)
+            vals[:, j] |= bit.astype(np.int64) << b
+            k += 1
+    return vals
+
+
+def book_codes(book: dict, words, d: int):
+    """Codes of packed records under a decode book, as indices into
+    book_table(book): plain codes for a uniform book; for a split book
+    (n_wide > 0) the narrow coordinates' codes are offset past the wide
+    codebook's entries, so that one table lookup gives every coordinate its
+    own width's centroid."""
+    nw = book.get("n_wide", 0)
+    if not nw:
+        return unpack_bits(words, d, book["bits"])
+    idx = unpack_bits_widths(words, split_widths(d, book["bits"], nw))
+    idx[..., nw:] += 1 << (book["bits"] + 1)
+    return idx
+
+
+def book_table(book: dict) -> np.ndarray:
+    """Centroid table that book_codes indexes (the wide then the narrow
+    codebook for a split book)."""
+    if not book.get("n_wide", 0):
+        return np.asarray(book["centroids"], dtype=np.float64)
+    return np.concatenate((np.asarray(book["wide"][0], dtype=np.float64),
+                           np.asarray(book["narrow"][0], dtype=np.float64)))
