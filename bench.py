@@ -118,10 +118,15 @@ def main():
     if args.config == "all":
         line = bench_bulk(args, T, dev, cpu=not args.no_cpu_baseline)
         subs = {}
-        for name in ("tiny", "llama8b", "batched2", "batched4", "llama70b"):
+        # split widths on the 8B layer: 3.5 bits (keys 2.5-bit codes + QJL,
+        # values 3.5-bit codes) and 2.5 bits (1.5 + QJL, 2.5)
+        splits = {"llama8b_split_3.5bit": (2, 3), "llama8b_split_2.5bit": (1, 2)}
+        for name in ("tiny", "llama8b", "batched2", "batched4", "llama70b", *splits):
             t0 = time.time()
             if name == "tiny":
                 rec = bench_tiny(args, T, dev)
+            elif name in splits:
+                rec = bench_layer(args, T, dev, "llama8b", logits=True, cpu=False, split=splits[name])
             else:
                 rec = bench_layer(args, T, dev, name, append_steps=8 if name.startswith("batched") else 0,
                                   chunk=args.chunk if name == "llama8b" else 0, logits=True, cpu=False)
@@ -150,9 +155,12 @@ def sub_record(line):
     return {k: v for k, v in line.items() if k not in _SUB_DROP}
 
 
-def bench_layer(args, T, dev, name, append_steps=0, chunk=0, logits=True, cpu=True):
+def bench_layer(args, T, dev, name, append_steps=0, chunk=0, logits=True, cpu=True, split=None):
     """One layer-shaped workload (8B, batched, 70B): encode all of its K and V,
-    then one decode over a full cache replica, per step."""
+    then one decode over a full cache replica, per step.  split = (key code
+    bits b', value bits b'): split widths instead of the workload's widths,
+    rotated coordinates 0..63 one bit wider (b' + 0.5 bits per coordinate,
+    keys plus their 1-bit QJL sketch)."""
     import torch
     t0 = time.time()
     wl = workload(name)
@@ -163,8 +171,15 @@ def bench_layer(args, T, dev, name, append_steps=0, chunk=0, logits=True, cpu=Tr
     if args.key_mode == "mse":
         kbits_mse = wl.k_bits
     qjl_m = 128 if args.key_mode == "qjl" else 0
-    kcb = T.Codebook(128, kbits_mse, qjl_m, 0, 1, device=0)
-    vcb = T.Codebook(128, wl.v_bits, 0, 0, 1, device=0)
+    tag = wl.name
+    if split is None:
+        kcb = T.Codebook(128, kbits_mse, qjl_m, 0, 1, device=0)
+        vcb = T.Codebook(128, wl.v_bits, 0, 0, 1, device=0)
+    else:
+        kbits_mse, vbits = split
+        kcb = T.Codebook(128, kbits_mse, qjl_m, 0, 1, device=0, wide_coords=64)
+        vcb = T.Codebook(128, vbits, 0, 0, 1, device=0, wide_coords=64)
+        tag = f"{wl.name}-split-k{kbits_mse + 0.5 + (1 if qjl_m else 0)}-v{vbits + 0.5}"
     n_vec = B * Hkv * S
 
     def up(a):
@@ -265,7 +280,10 @@ def bench_layer(args, T, dev, name, append_steps=0, chunk=0, logits=True, cpu=Tr
         "data": "synthetic",
         "config": {
             "workload": wl.name, "batch": B, "seq_len": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
-            "key_bits": wl.k_bits, "value_bits": wl.v_bits, "qjl_dim": qjl_m, "input_dtype": "bf16",
+            "key_bits": wl.k_bits if split is None else kbits_mse + 0.5 + (1 if qjl_m else 0),
+            "value_bits": wl.v_bits if split is None else split[1] + 0.5, "qjl_dim": qjl_m, "input_dtype": "bf16",
+            "split_widths": None if split is None else
+            {"wide_coords": 64, "key_code_bits": [kbits_mse + 1, kbits_mse], "value_code_bits": [split[1] + 1, split[1]]},
             "key_mode": "(b-1)-bit codes + 1-bit QJL" if qjl_m else "b-bit MSE-only codes",
             "step": "encode all K and V of the layer, then one decode step over a full cache",
             "cold_replicas": {"inputs": n_in, "caches": n_cache, "hot": bool(args.hot)},
@@ -277,9 +295,9 @@ def bench_layer(args, T, dev, name, append_steps=0, chunk=0, logits=True, cpu=Tr
         "roofline": {
             "kernel": "encode (keys: rotation + QJL)" if qjl_m else "encode (keys: rotation, MSE-only)", "bound": "hbm",
             "achieved": round(enc_k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4), "traffic": encode_traffic(wl.name) if qjl_m else None,
+            "frac": round(enc_k_gbps / HBM_PEAK_GBPS, 4), "traffic": encode_traffic(tag) if qjl_m else None,
             "algorithmic_bytes_per_launch": enc_k_bytes, "avg_launch_us": round(float(enc_k.mean()) * 1e3, 2),
-            "mfma": key_encode_mfma(n_vec, qjl_m, True, float(enc_k.mean()), wl.name),
+            "mfma": key_encode_mfma(n_vec, qjl_m, True, float(enc_k.mean()), tag),
         },
         "roofline_values_encode": {
             "bound": "hbm", "achieved": round(enc_v_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -290,7 +308,7 @@ def bench_layer(args, T, dev, name, append_steps=0, chunk=0, logits=True, cpu=Tr
             "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": dec_bytes,
             "avg_us_partial_and_combine": round(dec_ms * 1e3, 2),
-            "alu": decode_alu_view(B * Hq * S, qjl_m, dec_ms),
+            "mfma": decode_mfma_view(B * Hkv * S, Hq // Hkv, qjl_m, dec_ms),
         },
         "wall_s_timed": round(wall, 4),
         "launch_us_percentiles": {
@@ -396,7 +414,7 @@ def bench_bulk(args, T, dev, cpu=True):
                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "algorithmic_bytes_per_launch": enc_v_bytes},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes_per_launch": dec_bytes,
-                            "alu": decode_alu_view(Hq * Tlen, 128, float(dec.mean()))},
+                            "mfma": decode_mfma_view(Hkv * Tlen, Hq // Hkv, 128, float(dec.mean()))},
     }
     if cpu:
         line["cpu_baseline"] = cpu_baseline_bulk(kx, vx, q, args.cpu_seconds)
@@ -461,19 +479,24 @@ def bench_tiny(args, T, dev):
     }
 
 
-# Non-packed fp32 vector FMA issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-# (78.6 TFLOP/s counting an FMA as two flops; packed fp32 is not built).
-ALU_PEAK_T_FMA = 39.3216
+# Dense fp16 / bf16 MFMA peak of MI355X (TFLOP/s).
+MFMA_PEAK_TFLOPS = 2500.0
 
 
-def decode_alu_view(token_heads, qjl_m, ms):
-    """The decode against the vector-ALU roof: per (token, q head) the method
-    needs d multiply-adds for the codebook dot product, m for the sign term and
-    d for the value sum (384 at d = m = 128), as fp32 lane FMAs per second."""
-    fma = token_heads * (128 + qjl_m + 128)
-    achieved = fma / (ms * 1e-3) / 1e12
-    return {"bound": "alu", "achieved": round(achieved, 2), "peak": ALU_PEAK_T_FMA, "unit": "T FMA/s (fp32 lanes)",
-            "frac": round(achieved / ALU_PEAK_T_FMA, 4), "algorithmic_fma_per_launch": fma}
+def decode_mfma_view(kv_token_rows, g, qjl_m, ms):
+    """The matrix-core decode against the dense fp16/bf16 MFMA roof.  Per 16
+    tokens of one kv head it issues 8 key products, 4 sign products (QJL keys)
+    and 8 value products of v_mfma_f32_16x16x32 (16384 flops each), with the
+    g <= 8 heads' hi and lo parts in 16 columns; the method itself needs
+    2 (d + m + d) flops per (token, q head)."""
+    issued = kv_token_rows * (16 + (4 if qjl_m else 0)) * 16384 / 16
+    algorithmic = kv_token_rows * g * 2 * (128 + qjl_m + 128)
+    t = ms * 1e-3
+    return {"bound": "mfma", "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "achieved_issued": round(issued / t / 1e12, 1), "frac_issued": round(issued / t / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "achieved_algorithmic": round(algorithmic / t / 1e12, 1),
+            "frac_algorithmic": round(algorithmic / t / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "flops_per_launch_issued": float(issued), "flops_per_launch_algorithmic": float(algorithmic)}
 
 
 def cpu_baseline_bulk(kx, vx, q, min_seconds):

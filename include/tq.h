@@ -23,6 +23,9 @@
  *  - Packed codes: code j of a vector occupies bits [j*b', (j+1)*b') of the
  *    vector's bit stream, least significant bit first; stream bit k is bit
  *    k%32 of little-endian uint32 word k/32.  A vector has d*b'/32 code words.
+ *    With split widths (tq_codebook_build_split) code j starts at bit
+ *    sum_{i<j} width_i instead: the first w coordinates are b'+1 bits wide,
+ *    and a vector has (d*b' + w)/32 code words.
  *    Sign bit i (= [p_i > 0]) is stream bit i of the vector's m/32 sign words.
  *  - Cache layout (structure of arrays, all device memory, row-major):
  *      codes[B][H_kv][t_cap][d*b'/32]  uint32
@@ -85,6 +88,37 @@ tq_status tq_codebook_build(int32_t head_dim, int32_t mse_bits, int32_t qjl_dim,
                             uint64_t rot_seed, uint64_t qjl_seed, int32_t device,
                             tq_codebook **out);
 
+/* Split bit widths [cc-newplayer explainer, technical breakdown item 1: an
+ * average of about 2.5 bits per element; intelliparadigm "3-bit" article,
+ * §2.1 (a 2.5-bit intermediate) and §5.1 (3.5 bits)]: the pages give
+ * fractional averages without their construction; here rotated coordinates
+ * 0 .. wide_coords - 1 take the (mse_bits + 1)-bit Lloyd-Max codebook of f_d
+ * and the others the mse_bits-bit one, for mse_bits + wide_coords/d bits per
+ * coordinate (keys add their 1-bit sketch).  Every rotated coordinate follows
+ * f_d, so the expected distortion is the coordinate-weighted mean of the two
+ * widths' distortions whichever coordinates are wide.
+ *   mse_bits      b' in 1..3 when wide_coords > 0.
+ *   wide_coords   0 (a uniform codebook, as tq_codebook_build) .. d; the GPU
+ *                 path supports 0 and 64 (else TQ_ERR_UNSUPPORTED).
+ * Other arguments as in tq_codebook_build; Pi and S are the same for the same
+ * seeds.  Records pack the codes at running offsets (see the top).  On the
+ * GPU a split codebook encodes (tq_encode_kv, tq_append_decode) and is read by
+ * the single-query matrix-core decode: tq_decode_attention(_static),
+ * tq_append_decode and tq_attention_logits with t_cap a multiple of 4 and
+ * 16-byte aligned norm arrays, the key and value codebooks both split; other
+ * reads (chunks of several queries, other t_cap) return TQ_ERR_UNSUPPORTED. */
+tq_status tq_codebook_build_split(int32_t head_dim, int32_t mse_bits, int32_t wide_coords, int32_t qjl_dim,
+                                  uint64_t rot_seed, uint64_t qjl_seed, int32_t device, tq_codebook **out);
+
+/* wide_coords and the wide width (mse_bits + 1, or 0 for a uniform codebook);
+ * either pointer may be NULL. */
+tq_status tq_codebook_split_info(const tq_codebook *cb, int32_t *wide_coords, int32_t *wide_bits);
+
+/* The wide codebook's fp32 centroids[2L] and thresholds[2L-1] (host pointers,
+ * either may be NULL); TQ_ERR_INVALID_ARG for a uniform codebook.
+ * tq_codebook_export gives the b'-bit codebook of the other coordinates. */
+tq_status tq_codebook_export_wide(const tq_codebook *cb, float *centroids, float *thresholds);
+
 /* Release a handle (NULL is accepted).  The caller must make sure no enqueued
  * work still uses it. */
 tq_status tq_codebook_free(tq_codebook *cb);
@@ -103,7 +137,8 @@ tq_status tq_codebook_export(const tq_codebook *cb, float *centroids, float *thr
 tq_status tq_codebook_export_f64(const tq_codebook *cb, double *centroids, double *thresholds,
                                  double *rotation, double *qjl);
 
-/* Words per cache row: code_words = d*b'/32, sign_words = m/32 (either may be NULL). */
+/* Words per cache row: code_words = (d*b' + wide_coords)/32 rounded up,
+ * sign_words = m/32 (either may be NULL). */
 tq_status tq_record_words(const tq_codebook *cb, int32_t *code_words, int32_t *sign_words);
 
 /* Encode n vectors online into cache rows [memory-wall article §2: stage one
@@ -114,7 +149,7 @@ tq_status tq_record_words(const tq_codebook *cb, int32_t *code_words, int32_t *s
  *                 for row i -> cache row i.  Rows whose destination lies outside
  *                 [0, cache_rows) are skipped (nothing written).
  *   cache_rows    number of rows the output arrays hold (>= n when dst_row == NULL).
- *   codes         device uint32[cache_rows][d*b'/32].
+ *   codes         device uint32[cache_rows][code_words] (tq_record_words).
  *   signs         device uint32[cache_rows][m/32]; NULL iff m == 0.
  *   norms         device float[cache_rows]: nu = ||x||.
  *   res_norms     device float[cache_rows]: gamma = ||y - c[idx]||; NULL iff m == 0.
@@ -123,7 +158,8 @@ tq_status tq_record_words(const tq_codebook *cb, int32_t *code_words, int32_t *s
  *   dbg_proj      NULL, or device float[n][m]: p = S r exactly as signed (m > 0).
  * Per vector: nu = ||x||; y = Pi x / nu (y = 0 when nu == 0); code_j =
  * #{i : y_j >= t_i} (NaN -> 0); keys: r = y - c[code], gamma = ||r||,
- * sign_i = [ (S r)_i > 0 ].  Pure function of (x, codebook): re-running it on
+ * sign_i = [ (S r)_i > 0 ].  With split widths coordinate j uses its own
+ * width's thresholds and centroids.  Pure function of (x, codebook): re-running it on
  * the same rows is idempotent.  n == 0 is a no-op. */
 tq_status tq_encode_kv(const tq_codebook *cb, const void *x, tq_dtype x_dtype, int64_t n,
                        int64_t x_row_stride, const int64_t *dst_row, int64_t cache_rows,

@@ -21,7 +21,8 @@ TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_ALLOC, TQ_ERR_DEVICE = 0, 
 TQ_F32, TQ_BF16 = 0, 1
 
 EXPORTED = (
-    "tq_codebook_build", "tq_codebook_free", "tq_codebook_info", "tq_codebook_export",
+    "tq_codebook_build", "tq_codebook_build_split", "tq_codebook_split_info", "tq_codebook_export_wide",
+    "tq_codebook_free", "tq_codebook_info", "tq_codebook_export",
     "tq_codebook_export_f64", "tq_record_words", "tq_encode_kv", "tq_decode_workspace_bytes",
     "tq_decode_attention", "tq_decode_attention_static", "tq_append_decode", "tq_attention_logits", "tq_chunk_attention",
     "tq_chunk_workspace_bytes", "tq_status_string", "tq_last_error",
@@ -53,6 +54,9 @@ def load_library() -> ctypes.CDLL:
     vp, i32, i64, u64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
     pi32 = ctypes.POINTER(ctypes.c_int32)
     lib.tq_codebook_build.argtypes = [i32, i32, i32, u64, u64, i32, ctypes.POINTER(vp)]
+    lib.tq_codebook_build_split.argtypes = [i32, i32, i32, i32, u64, u64, i32, ctypes.POINTER(vp)]
+    lib.tq_codebook_split_info.argtypes = [vp, pi32, pi32]
+    lib.tq_codebook_export_wide.argtypes = [vp, vp, vp]
     lib.tq_codebook_free.argtypes = [vp]
     lib.tq_codebook_info.argtypes = [vp, pi32, pi32, pi32, pi32]
     lib.tq_codebook_export.argtypes = [vp, vp, vp, vp, vp]
@@ -102,16 +106,23 @@ class Codebook:
     """Setup tables of one quantizer: Lloyd-Max codebook, rotation, QJL matrix.
 
     device=-1 builds a host-only handle (export works, encode/decode do not).
+    wide_coords > 0 builds split widths (tq_codebook_build_split): rotated
+    coordinates 0 .. wide_coords - 1 on the (mse_bits + 1)-bit codebook.
     """
 
     def __init__(self, head_dim: int = 128, mse_bits: int = 2, qjl_dim: int = 0,
-                 rot_seed: int = 0, qjl_seed: int = 1, device: int = 0):
+                 rot_seed: int = 0, qjl_seed: int = 1, device: int = 0, wide_coords: int = 0):
         lib = load_library()
         h = ctypes.c_void_p()
-        _check(lib.tq_codebook_build(head_dim, mse_bits, qjl_dim, rot_seed, qjl_seed, device, ctypes.byref(h)),
-               "tq_codebook_build")
+        if wide_coords:
+            _check(lib.tq_codebook_build_split(head_dim, mse_bits, wide_coords, qjl_dim, rot_seed, qjl_seed, device,
+                                               ctypes.byref(h)), "tq_codebook_build_split")
+        else:
+            _check(lib.tq_codebook_build(head_dim, mse_bits, qjl_dim, rot_seed, qjl_seed, device, ctypes.byref(h)),
+                   "tq_codebook_build")
         self._h = h
         self.head_dim, self.mse_bits, self.qjl_dim, self.device = head_dim, mse_bits, qjl_dim, device
+        self.wide_coords = wide_coords
         self.rot_seed, self.qjl_seed = rot_seed, qjl_seed
         cw, sw = ctypes.c_int32(), ctypes.c_int32()
         _check(lib.tq_record_words(h, ctypes.byref(cw), ctypes.byref(sw)), "tq_record_words")
@@ -148,6 +159,21 @@ class Codebook:
         _check(fn(self.handle, c.ctypes.data, t.ctypes.data, rot.ctypes.data,
                   None if qjl is None else qjl.ctypes.data), "tq_codebook_export")
         return {"centroids": c, "thresholds": t, "rotation": rot, "qjl": qjl}
+
+    def split_info(self) -> tuple:
+        """(wide_coords, wide_bits) as the library reports them ((0, 0) when uniform)."""
+        wc, wb = ctypes.c_int32(), ctypes.c_int32()
+        _check(load_library().tq_codebook_split_info(self.handle, ctypes.byref(wc), ctypes.byref(wb)),
+               "tq_codebook_split_info")
+        return wc.value, wb.value
+
+    def export_wide(self) -> dict:
+        """The wide codebook's fp32 centroids and thresholds (split widths only)."""
+        L = 1 << (self.mse_bits + 1)
+        c, t = np.zeros(L, np.float32), np.zeros(L - 1, np.float32)
+        _check(load_library().tq_codebook_export_wide(self.handle, c.ctypes.data, t.ctypes.data),
+               "tq_codebook_export_wide")
+        return {"centroids": c, "thresholds": t}
 
 
 @dataclass

@@ -171,13 +171,24 @@ tq_status upload_tables(tq_codebook *cb) {
   off = align256(off + tq::kMValLutBytes);
   cb->off_sign_lut = off;
   off = align256(off + tq::kSignLutBytes);
+  const bool split = h.n_wide > 0;
+  if (split) {
+    cb->off_qcells_w = off;
+    off = align256(off + tq::kQuantCellEntries * 4 * sizeof(float));
+    cb->off_mkey_lut_w = off;
+    off = align256(off + tq::kMKeyLutBytes);
+    cb->off_mval_lut_w = off;
+    off = align256(off + tq::kMValLutBytes);
+  }
   cb->dev_bytes = off;
 
   std::vector<unsigned char> img(off, 0);
   std::memcpy(img.data() + cb->off_centroids, h.centroids.data(), h.centroids.size() * sizeof(float));
   std::memcpy(img.data() + cb->off_thresholds, h.thresholds.data(), h.thresholds.size() * sizeof(float));
-  tq::pack_encode_fragments(h.rotation.data(), img.data() + cb->off_rot_frag);
-  if (m > 0) tq::pack_encode_fragments(h.qjl.data(), img.data() + cb->off_qjl_frag);
+  // split widths: Pi's output rows and S's input columns follow the encode's
+  // split coordinate order (the wide coordinates in blocks 0..3)
+  tq::pack_encode_fragments(h.rotation.data(), img.data() + cb->off_rot_frag, split, false);
+  if (m > 0) tq::pack_encode_fragments(h.qjl.data(), img.data() + cb->off_qjl_frag, false, split);
   std::memcpy(img.data() + cb->off_rot_f32, h.rotation.data(), h.rotation.size() * sizeof(float));
   float *rt = reinterpret_cast<float *>(img.data() + cb->off_rot_t_f32);
   for (int i = 0; i < d; ++i)
@@ -194,25 +205,22 @@ tq_status upload_tables(tq_codebook *cb) {
         st[i * m + r] = static_cast<float>(v);
       }
   }
-  {
-    // Matrix-core decode operand tables (layouts in tq_kernels.h): centroid
-    // value c as (hi, lo) = (bf16(c), bf16(c - hi)), two per 32-bit word.
-    const int b = h.bits, mask = (1 << b) - 1;
-    std::vector<uint16_t> hi(h.levels), lo(h.levels);
-    for (int k = 0; k < h.levels; ++k) {
-      hi[k] = tq::bf16_bits_rne(h.centroids[k]);
-      lo[k] = tq::bf16_bits_rne(h.centroids[k] - tq::bf16_bits_to_float(hi[k]));
-    }
-    auto pair = [](uint16_t x, uint16_t y) { return static_cast<uint32_t>(x) | (static_cast<uint32_t>(y) << 16); };
-    // keys: fp16 (hi, lo) of 256 c (the score products run in fp16)
-    std::vector<uint16_t> khi(h.levels), klo(h.levels);
-    for (int k = 0; k < h.levels; ++k) {
-      const float x = 256.0f * h.centroids[k];
+  auto pair = [](uint16_t x, uint16_t y) { return static_cast<uint32_t>(x) | (static_cast<uint32_t>(y) << 16); };
+  // Matrix-core decode operand tables of one codebook (layouts in
+  // tq_kernels.h): centroid c as (hi, lo) with lo = c - hi, two per 32-bit word.
+  auto operand_tables = [&](const std::vector<float> &cent, int b, size_t off_k, size_t off_v) {
+    const int levels = 1 << b, mask = levels - 1;
+    std::vector<uint16_t> hi(levels), lo(levels), khi(levels), klo(levels);
+    for (int k = 0; k < levels; ++k) {
+      hi[k] = tq::bf16_bits_rne(cent[k]);
+      lo[k] = tq::bf16_bits_rne(cent[k] - tq::bf16_bits_to_float(hi[k]));
+      // keys: fp16 (hi, lo) of 256 c (the score products run in fp16)
+      const float x = 256.0f * cent[k];
       khi[k] = f16_bits_rne(x);
       klo[k] = f16_bits_rne(x - f16_bits_to_float(khi[k]));
     }
-    uint32_t *mk = reinterpret_cast<uint32_t *>(img.data() + cb->off_mkey_lut);
-    uint32_t *mv = reinterpret_cast<uint32_t *>(img.data() + cb->off_mval_lut);
+    uint32_t *mk = reinterpret_cast<uint32_t *>(img.data() + off_k);
+    uint32_t *mv = reinterpret_cast<uint32_t *>(img.data() + off_v);
     for (int e = 0; e < (1 << (2 * b)); ++e) {
       const int c0 = e & mask, c1 = (e >> b) & mask;
       mk[2 * e] = pair(khi[c0], klo[c0]);
@@ -220,6 +228,10 @@ tq_status upload_tables(tq_codebook *cb) {
       mv[2 * e] = pair(hi[c0], lo[c0]);   // values: bf16 (hi, lo) of c
       mv[2 * e + 1] = pair(hi[c1], lo[c1]);
     }
+  };
+  operand_tables(h.centroids, h.bits, cb->off_mkey_lut, cb->off_mval_lut);
+  if (split) operand_tables(h.wide_centroids, h.bits + 1, cb->off_mkey_lut_w, cb->off_mval_lut_w);
+  {
     uint32_t *sg = reinterpret_cast<uint32_t *>(img.data() + cb->off_sign_lut);
     const uint16_t plus = 0x3C00, minus = 0xBC00;   // fp16 +1, -1
     for (int e = 0; e < 256; ++e)
@@ -241,6 +253,13 @@ tq_status upload_tables(tq_codebook *cb) {
   if (!tq::build_quant_cells(h.thresholds.data(), h.centroids.data(), h.levels,
                              reinterpret_cast<float *>(img.data() + cb->off_qcells), &cb->qscale, &cb->qbias))
     return fail(TQ_ERR_UNSUPPORTED, "codebook thresholds do not fit the quantizer cell grid");
+  if (split) {
+    float qs = 0.f, qb = 0.f;
+    if (!tq::build_quant_cells(h.wide_thresholds.data(), h.wide_centroids.data(), 2 * h.levels,
+                               reinterpret_cast<float *>(img.data() + cb->off_qcells_w), &qs, &qb) ||
+        qs != cb->qscale || qb != cb->qbias)
+      return fail(TQ_ERR_UNSUPPORTED, "wide codebook thresholds do not fit the quantizer cell grid");
+  }
   DeviceGuard guard(cb->device);
   if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice(%d): %s", cb->device, hipGetErrorString(guard.err));
   hipError_t e = hipMalloc(&cb->dev_buf, off);
@@ -258,12 +277,8 @@ const T *dev_ptr(const tq_codebook *cb, size_t off) {
   return reinterpret_cast<const T *>(static_cast<const unsigned char *>(cb->dev_buf) + off);
 }
 
-}  // namespace
-
-extern "C" {
-
-tq_status tq_codebook_build(int32_t head_dim, int32_t mse_bits, int32_t qjl_dim, uint64_t rot_seed,
-                            uint64_t qjl_seed, int32_t device, tq_codebook **out) {
+tq_status build_codebook(int32_t head_dim, int32_t mse_bits, int32_t wide_coords, int32_t qjl_dim, uint64_t rot_seed,
+                         uint64_t qjl_seed, int32_t device, tq_codebook **out) {
   if (out == nullptr) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (device < -1) return fail(TQ_ERR_INVALID_ARG, "device must be >= -1");
@@ -272,6 +287,9 @@ tq_status tq_codebook_build(int32_t head_dim, int32_t mse_bits, int32_t qjl_dim,
       return fail(TQ_ERR_UNSUPPORTED, "the GPU path supports head_dim 128 only (got %d)", head_dim);
     if (qjl_dim != 0 && qjl_dim != tq::kQjlDim)
       return fail(TQ_ERR_UNSUPPORTED, "the GPU path supports qjl_dim 0 or 128 only (got %d)", qjl_dim);
+    if (wide_coords != 0 && wide_coords != tq::kSplitWide)
+      return fail(TQ_ERR_UNSUPPORTED, "the GPU path supports wide_coords 0 or %d only (got %d)", tq::kSplitWide,
+                  wide_coords);
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || device >= count)
       return fail(TQ_ERR_INVALID_ARG, "device %d not present (%d devices)", device, count);
@@ -279,7 +297,7 @@ tq_status tq_codebook_build(int32_t head_dim, int32_t mse_bits, int32_t qjl_dim,
   tq_codebook *cb = new (std::nothrow) tq_codebook();
   if (cb == nullptr) return fail(TQ_ERR_ALLOC, "host allocation failed");
   std::string err;
-  if (!tq::build_host_tables(head_dim, mse_bits, qjl_dim, rot_seed, qjl_seed, &cb->host, &err)) {
+  if (!tq::build_host_tables(head_dim, mse_bits, wide_coords, qjl_dim, rot_seed, qjl_seed, &cb->host, &err)) {
     delete cb;
     return fail(TQ_ERR_INVALID_ARG, "%s", err.c_str());
   }
@@ -296,6 +314,36 @@ tq_status tq_codebook_build(int32_t head_dim, int32_t mse_bits, int32_t qjl_dim,
     }
   }
   *out = cb;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_codebook_build(int32_t head_dim, int32_t mse_bits, int32_t qjl_dim, uint64_t rot_seed,
+                            uint64_t qjl_seed, int32_t device, tq_codebook **out) {
+  return build_codebook(head_dim, mse_bits, 0, qjl_dim, rot_seed, qjl_seed, device, out);
+}
+
+tq_status tq_codebook_build_split(int32_t head_dim, int32_t mse_bits, int32_t wide_coords, int32_t qjl_dim,
+                                  uint64_t rot_seed, uint64_t qjl_seed, int32_t device, tq_codebook **out) {
+  return build_codebook(head_dim, mse_bits, wide_coords, qjl_dim, rot_seed, qjl_seed, device, out);
+}
+
+tq_status tq_codebook_split_info(const tq_codebook *cb, int32_t *wide_coords, int32_t *wide_bits) {
+  if (cb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  if (wide_coords) *wide_coords = cb->host.n_wide;
+  if (wide_bits) *wide_bits = cb->host.n_wide > 0 ? cb->host.bits + 1 : 0;
+  return ok();
+}
+
+tq_status tq_codebook_export_wide(const tq_codebook *cb, float *centroids, float *thresholds) {
+  if (cb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
+  const tq::HostTables &h = cb->host;
+  if (h.n_wide == 0) return fail(TQ_ERR_INVALID_ARG, "the codebook has no wide coordinates");
+  if (centroids) std::memcpy(centroids, h.wide_centroids.data(), h.wide_centroids.size() * sizeof(float));
+  if (thresholds) std::memcpy(thresholds, h.wide_thresholds.data(), h.wide_thresholds.size() * sizeof(float));
   return ok();
 }
 
@@ -346,7 +394,7 @@ tq_status tq_codebook_export_f64(const tq_codebook *cb, double *centroids, doubl
 
 tq_status tq_record_words(const tq_codebook *cb, int32_t *code_words, int32_t *sign_words) {
   if (cb == nullptr) return fail(TQ_ERR_INVALID_ARG, "codebook is NULL");
-  const int bitsum = cb->host.d * cb->host.bits;
+  const int bitsum = cb->host.d * cb->host.bits + cb->host.n_wide;
   if (code_words) *code_words = (bitsum + 31) / 32;
   if (sign_words) *sign_words = cb->host.m / 32;
   return ok();
@@ -395,6 +443,7 @@ tq_status prepare_encode(const tq_codebook *cb, const void *x, tq_dtype x_dtype,
   a.frag_rot = dev_ptr<uint4>(cb, cb->off_rot_frag);
   a.frag_qjl = (m > 0) ? dev_ptr<uint4>(cb, cb->off_qjl_frag) : nullptr;
   a.qlut = dev_ptr<float4>(cb, cb->off_qcells);
+  a.qlut_wide = cb->host.n_wide > 0 ? dev_ptr<float4>(cb, cb->off_qcells_w) : nullptr;
   a.qscale = cb->qscale;
   a.qbias = cb->qbias;
   *out = a;
@@ -404,8 +453,8 @@ tq_status prepare_encode(const tq_codebook *cb, const void *x, tq_dtype x_dtype,
 tq_status run_encode(const tq_codebook *cb, const tq::EncodeArgs &a, bool x_f32, void *stream) {
   DeviceGuard guard(cb->device);
   if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
-  hipError_t e = tq::launch_encode(a, cb->host.bits, cb->host.m > 0, x_f32, cu_count(cb->device),
-                                   static_cast<hipStream_t>(stream));
+  hipError_t e = tq::launch_encode(a, cb->host.bits, cb->host.m > 0, x_f32, cb->host.n_wide > 0,
+                                   cu_count(cb->device), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "encode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -498,7 +547,12 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
   a.k_pair = dev_ptr<float>(kcb, kcb->off_pair_lut);
   a.mk_lut = dev_ptr<void>(kcb, kcb->off_mkey_lut);
   a.sg_lut = dev_ptr<void>(kcb, kcb->off_sign_lut);
+  a.k_split = kcb->host.n_wide > 0;
+  a.mk_lut_w = a.k_split ? dev_ptr<void>(kcb, kcb->off_mkey_lut_w) : nullptr;
   a.norm_vec4 = (k->t_cap % 4 == 0) && aligned(k->norms, 16) && (k->res_norms == nullptr || aligned(k->res_norms, 16));
+  if (a.k_split && !(n_new == 1 && a.norm_vec4 && a.t_cap <= tq::kMDecodeMaxTcap))
+    return fail(TQ_ERR_UNSUPPORTED, "split-width keys are read by the single-query matrix-core decode only: "
+                "n_new 1, t_cap a multiple of 4, 16-byte aligned norm arrays");
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   a.ws_qslot = reinterpret_cast<float *>(ws + plan.off_qslot);
   a.ws_part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
@@ -540,7 +594,15 @@ tq_status prepare_decode(const tq_codebook *kcb, const tq_codebook *vcb, const v
   a.rot_v = dev_ptr<float>(vcb, vcb->off_rot_f32);
   a.v_lut = dev_ptr<float>(vcb, vcb->off_pair_lut);
   a.mv_lut = dev_ptr<void>(vcb, vcb->off_mval_lut);
+  a.v_split = vcb->host.n_wide > 0;
+  a.mv_lut_w = a.v_split ? dev_ptr<void>(vcb, vcb->off_mval_lut_w) : nullptr;
   a.norm_vec4 = a.norm_vec4 && aligned(v->norms, 16);
+  if (a.k_split != a.v_split)
+    return fail(TQ_ERR_UNSUPPORTED, "split widths need both codebooks split (keys %d, values %d wide coordinates)",
+                kcb->host.n_wide, vcb->host.n_wide);
+  if (a.v_split && !tq::mdecode_applies(a))
+    return fail(TQ_ERR_UNSUPPORTED, "split-width values are read by the single-query matrix-core decode only: "
+                "t_cap a multiple of 4, 16-byte aligned norm arrays");
   *out_args = a;
   return ok();
 }
@@ -646,7 +708,7 @@ tq_status tq_append_decode(const tq_codebook *kcb, const tq_codebook *vcb, const
   }
   da.seq_add = 1;
   da.seq_inc = seq_len;
-  if (kv_dtype == TQ_BF16) {
+  if (kv_dtype == TQ_BF16 && kcb->host.n_wide == 0 && vcb->host.n_wide == 0) {
     // keys and values side by side in one launch
     DeviceGuard guard(kcb->device);
     if (guard.err != hipSuccess) return fail(TQ_ERR_DEVICE, "hipSetDevice: %s", hipGetErrorString(guard.err));
@@ -654,8 +716,8 @@ tq_status tq_append_decode(const tq_codebook *kcb, const tq_codebook *vcb, const
                                                 cu_count(kcb->device), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "append encode launch: %s", hipGetErrorString(e));
   } else {
-    if ((st = run_encode(kcb, ka, true, stream)) != TQ_OK) return st;
-    if ((st = run_encode(vcb, va, true, stream)) != TQ_OK) return st;
+    if ((st = run_encode(kcb, ka, kv_dtype == TQ_F32, stream)) != TQ_OK) return st;
+    if ((st = run_encode(vcb, va, kv_dtype == TQ_F32, stream)) != TQ_OK) return st;
   }
   return run_decode(kcb, da, stream);
 }

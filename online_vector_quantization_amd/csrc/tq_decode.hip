@@ -1121,7 +1121,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
 
 hipError_t launch_logits(const DecodeArgs &a, hipStream_t stream) {
   if (a.scores == nullptr) return hipErrorInvalidValue;
-  return launch_main<true>(a, stream);
+  // the key phase of the kernel launch_decode picks for the same arguments,
+  // so the logits equal the decode's own bit for bit
+  return mdecode_applies(a) ? launch_mdecode_main(a, true, stream) : launch_main<true>(a, stream);
 }
 
 }  // namespace tq

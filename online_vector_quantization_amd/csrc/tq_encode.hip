@@ -89,6 +89,20 @@ __device__ __forceinline__ void split_bf16(const f32x8 &v, bf16x8 &hi, bf16x8 &l
 }
 
 
+// out = the A low bits of (a1:a0) followed by the bits of (b1:b0), as four
+// words (A a multiple of 16 in 16..64).
+template <int A>
+__device__ __forceinline__ void concat_bits(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, uint32_t (&out)[4]) {
+  static_assert(A % 16 == 0 && A >= 16 && A <= 64, "A in 16..64, a multiple of 16");
+  const uint64_t a = (static_cast<uint64_t>(a1) << 32) | a0, b = (static_cast<uint64_t>(b1) << 32) | b0;
+  const uint64_t lo = (A == 64) ? a : (a & ((uint64_t{1} << A) - 1)) | (b << A);
+  const uint64_t hi = (A == 64) ? b : (b >> (64 - A));
+  out[0] = static_cast<uint32_t>(lo);
+  out[1] = static_cast<uint32_t>(lo >> 32);
+  out[2] = static_cast<uint32_t>(hi);
+  out[3] = static_cast<uint32_t>(hi >> 32);
+}
+
 // One lane's 32 input coordinates of one vector.
 template <bool XF32> struct XRegs;
 template <> struct XRegs<false> { uint4 w[4]; };
@@ -125,7 +139,7 @@ __device__ __forceinline__ int64_t dest_row(const EncodeArgs &a, int64_t vec, bo
 
 // The encode of work-group `block` of `nblocks` over the rows of `a`;
 // s_frag holds (QJL ? 4 : 2) fragment splits, s_qlut the cell table.
-template <int BITS, bool QJL, bool XF32, bool DBG>
+template <int BITS, bool QJL, bool XF32, bool DBG, bool SPLIT>
 __device__ __forceinline__ void encode_body(const EncodeArgs &a, uint4 *s_frag, float4 *s_qlut, int block,
                                             int nblocks) {
   constexpr int NT = kNT;
@@ -138,13 +152,13 @@ __device__ __forceinline__ void encode_body(const EncodeArgs &a, uint4 *s_frag, 
 #undef TQ_ENC_NBLOCKS
 }
 
-template <int BITS, bool QJL, bool XF32, bool DBG>
+template <int BITS, bool QJL, bool XF32, bool DBG, bool SPLIT>
 __global__ __launch_bounds__(EncGeom<QJL>::kThreads) void encode_kernel(EncodeArgs a) {
   constexpr int NT = kNT;
   constexpr int kWaves = EncGeom<QJL>::kWaves;
   constexpr int kThreads = EncGeom<QJL>::kThreads;
   __shared__ uint4 s_frag[(QJL ? 4 : 2) * kFragU4];
-  __shared__ float4 s_qlut[kQuantCellEntries];
+  __shared__ float4 s_qlut[(SPLIT ? 2 : 1) * kQuantCellEntries];
 
 #define TQ_ENC_BLOCK blockIdx.x
 #define TQ_ENC_NBLOCKS gridDim.x
@@ -163,9 +177,9 @@ __global__ __launch_bounds__(EncGeom<true>::kThreads) void encode_pair_kernel(En
   __shared__ uint4 s_frag[4 * kFragU4];
   __shared__ float4 s_qlut[kQuantCellEntries];
   if (static_cast<int>(blockIdx.x) < k_blocks) {
-    encode_body<KBITS, KQJL, false, false>(ka, s_frag, s_qlut, blockIdx.x, k_blocks);
+    encode_body<KBITS, KQJL, false, false, false>(ka, s_frag, s_qlut, blockIdx.x, k_blocks);
   } else {
-    encode_body<VBITS, false, false, false>(va, s_frag, s_qlut, blockIdx.x - k_blocks, gridDim.x - k_blocks);
+    encode_body<VBITS, false, false, false, false>(va, s_frag, s_qlut, blockIdx.x - k_blocks, gridDim.x - k_blocks);
   }
 }
 
@@ -193,28 +207,35 @@ hipError_t launch_pair_k(const EncodeArgs &ka, const EncodeArgs &va, int vbits, 
   return hipGetLastError();
 }
 
-template <int BITS, bool QJL, bool XF32>
+template <int BITS, bool QJL, bool XF32, bool SPLIT>
 hipError_t launch_t(const EncodeArgs &a, int num_cus, hipStream_t stream) {
   const int grid = encode_grid(a, QJL, num_cus);
   if (a.dbg_rot != nullptr || a.dbg_proj != nullptr)
-    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, true>), dim3(grid), dim3(EncGeom<QJL>::kThreads), 0, stream, a);
+    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, true, SPLIT>), dim3(grid), dim3(EncGeom<QJL>::kThreads), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, false>), dim3(grid), dim3(EncGeom<QJL>::kThreads), 0, stream, a);
+    hipLaunchKernelGGL((encode_kernel<BITS, QJL, XF32, false, SPLIT>), dim3(grid), dim3(EncGeom<QJL>::kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, bool SPLIT>
 hipError_t launch_bits(const EncodeArgs &a, bool qjl, bool x_f32, int num_cus, hipStream_t stream) {
-  if (qjl) return x_f32 ? launch_t<BITS, true, true>(a, num_cus, stream) : launch_t<BITS, true, false>(a, num_cus, stream);
-  return x_f32 ? launch_t<BITS, false, true>(a, num_cus, stream) : launch_t<BITS, false, false>(a, num_cus, stream);
+  if (qjl)
+    return x_f32 ? launch_t<BITS, true, true, SPLIT>(a, num_cus, stream)
+                 : launch_t<BITS, true, false, SPLIT>(a, num_cus, stream);
+  return x_f32 ? launch_t<BITS, false, true, SPLIT>(a, num_cus, stream)
+               : launch_t<BITS, false, false, SPLIT>(a, num_cus, stream);
 }
 
 }  // namespace
 
-void pack_encode_fragments(const float *mat, void *dst) {
+void pack_encode_fragments(const float *mat, void *dst, bool split_rows, bool split_cols) {
   // Element (t, s, lane, e) of a split is A[row][col] of the 16x16x32 MFMA tile
-  // t, k-step s: lane % 16 picks output row 32*((lane%16)/4) + 4t + (lane%4),
-  // element e with lane / 16 picks input column 32*(lane/16) + 8s + e.
+  // t, k-step s: lane % 16 picks output row enc_coord(i / 4, t, i % 4) with
+  // i = lane % 16 (the coordinate that lane group i / 4 receives), element e
+  // with lane / 16 picks input column enc_coord(lane / 16, 2s + e / 4, e % 4)
+  // (the coordinate that lane group holds as element e of its k-step s).
   uint16_t *out = static_cast<uint16_t *>(dst);
   for (int split = 0; split < 2; ++split)
     for (int t = 0; t < 8; ++t)
@@ -222,8 +243,8 @@ void pack_encode_fragments(const float *mat, void *dst) {
         for (int lane = 0; lane < 64; ++lane)
           for (int e = 0; e < 8; ++e) {
             const int i = lane & 15, kq = lane >> 4;
-            const int row = 32 * (i >> 2) + 4 * t + (i & 3);
-            const int col = 32 * kq + 8 * s + e;
+            const int row = enc_coord(split_rows, i >> 2, t, i & 3);
+            const int col = enc_coord(split_cols, kq, 2 * s + (e >> 2), e & 3);
             const float v = mat[row * kHeadDim + col];
             const uint16_t hi = bf16_bits_rne(v);
             const uint16_t val = split == 0 ? hi : bf16_bits_rne(v - bf16_bits_to_float(hi));
@@ -285,13 +306,23 @@ hipError_t launch_encode_pair(const EncodeArgs &ka, int kbits, bool kqjl, const 
   }
 }
 
-hipError_t launch_encode(const EncodeArgs &a, int bits, bool qjl, bool x_f32, int num_cus,
+hipError_t launch_encode(const EncodeArgs &a, int bits, bool qjl, bool x_f32, bool split, int num_cus,
                          hipStream_t stream) {
+  if (split) {
+    // b' + 1 <= 4 bits on the wide coordinates
+    if (a.qlut_wide == nullptr) return hipErrorInvalidValue;
+    switch (bits) {
+      case 1: return launch_bits<1, true>(a, qjl, x_f32, num_cus, stream);
+      case 2: return launch_bits<2, true>(a, qjl, x_f32, num_cus, stream);
+      case 3: return launch_bits<3, true>(a, qjl, x_f32, num_cus, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (bits) {
-    case 1: return launch_bits<1>(a, qjl, x_f32, num_cus, stream);
-    case 2: return launch_bits<2>(a, qjl, x_f32, num_cus, stream);
-    case 3: return launch_bits<3>(a, qjl, x_f32, num_cus, stream);
-    case 4: return launch_bits<4>(a, qjl, x_f32, num_cus, stream);
+    case 1: return launch_bits<1, false>(a, qjl, x_f32, num_cus, stream);
+    case 2: return launch_bits<2, false>(a, qjl, x_f32, num_cus, stream);
+    case 3: return launch_bits<3, false>(a, qjl, x_f32, num_cus, stream);
+    case 4: return launch_bits<4, false>(a, qjl, x_f32, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }

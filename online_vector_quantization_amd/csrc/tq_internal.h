@@ -16,10 +16,15 @@ struct HostTables {
   int d = 0, bits = 0, m = 0, levels = 0;
   std::vector<double> centroids64, thresholds64, rotation64, qjl64;
   std::vector<float> centroids, thresholds, rotation, qjl;
+  // Split widths: rotated coordinates 0 .. n_wide - 1 take the (bits + 1)-bit
+  // codebook below (empty when n_wide == 0), the others the bits-bit one above.
+  int n_wide = 0;
+  std::vector<double> wide_centroids64, wide_thresholds64;
+  std::vector<float> wide_centroids, wide_thresholds;
 };
 
 // Builds every host table; returns false (with `err` set) on bad input.
-bool build_host_tables(int d, int bits, int m, uint64_t rot_seed, uint64_t qjl_seed,
+bool build_host_tables(int d, int bits, int n_wide, int m, uint64_t rot_seed, uint64_t qjl_seed,
                        HostTables *out, std::string *err);
 
 // Pieces exposed for the CPU tests of the library's own setup code.
@@ -56,5 +61,10 @@ struct tq_codebook {
   size_t off_mkey_lut = 0;        // matrix-core decode: key operand table
   size_t off_mval_lut = 0;        // matrix-core decode: value operand table
   size_t off_sign_lut = 0;        // matrix-core decode: sign table
+  // Split widths: the wide codebook's encode cell table and matrix-core
+  // decode operand tables (0 when the codebook has no wide coordinates).
+  size_t off_qcells_w = 0;
+  size_t off_mkey_lut_w = 0;
+  size_t off_mval_lut_w = 0;
   float qscale = 0.f, qbias = 0.f;
 };

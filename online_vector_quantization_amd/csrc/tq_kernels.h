@@ -11,6 +11,19 @@ namespace tq {
 constexpr int kHeadDim = 128;    // the GPU path's d
 constexpr int kQjlDim = 128;     // the GPU path's m for keys
 constexpr int kMaxLevels = 16;   // 2^4
+// Split widths on the GPU path: rotated coordinates 0..63 take the
+// (b' + 1)-bit codebook, 64..127 the b'-bit one; a record holds the 64 wide
+// codes (at running offsets) and then the 64 narrow ones.
+constexpr int kSplitWide = 64;
+constexpr int split_code_words(int b) { return 2 * (2 * b + 1); }
+
+// Rotated coordinate that encode lane group kq (lane / 16) receives as element
+// e of output block t: 32 kq + 4 t + e, or with split widths 64 (t / 4) +
+// 16 kq + 4 (t % 4) + e, which puts the wide coordinates in blocks 0..3 and
+// the narrow ones in 4..7 of every lane.
+__host__ __device__ constexpr int enc_coord(bool split, int kq, int t, int e) {
+  return split ? 64 * (t >> 2) + 16 * kq + 4 * (t & 3) + e : 32 * kq + 4 * t + e;
+}
 
 // Encode operands are bf16 fragments laid out so that each lane of a wave
 // reads its 16-byte A operand of v_mfma_f32_16x16x32_bf16 with one LDS load:
@@ -44,12 +57,16 @@ struct EncodeArgs {
   const uint4 *frag_rot;   // kFragBytes
   const uint4 *frag_qjl;   // kFragBytes (keys with QJL)
   const float4 *qlut;      // kQuantCellEntries quantizer cells
+  const float4 *qlut_wide; // split widths: the wide codebook's cells (else null)
   float qscale, qbias;     // cell = min(uint(y * qscale + qbias), kQuantCellEntries - 1)
 };
 
 // Fills `dst` (kFragBytes) with the hi/lo bf16 fragments of the 128 x 128
-// row-major matrix `mat` (rows = outputs, columns = inputs).
-void pack_encode_fragments(const float *mat, void *dst);
+// row-major matrix `mat` (rows = outputs, columns = inputs).  split_rows puts
+// the output rows in the split coordinate order of enc_coord (the rotation's
+// outputs are the rotated coordinates); split_cols does so for the input
+// columns (S's inputs are the rotated residual's coordinates).
+void pack_encode_fragments(const float *mat, void *dst, bool split_rows, bool split_cols);
 
 // Builds the quantizer cell table (4 floats per cell); false if the
 // thresholds do not fit the cell grid (then the GPU path is unsupported).
@@ -57,7 +74,7 @@ bool build_quant_cells(const float *thresholds, const float *centroids, int leve
                        float *qscale, float *qbias);
 
 // Enqueues the encode kernel; returns the launch error (hipSuccess on success).
-hipError_t launch_encode(const EncodeArgs &a, int bits, bool qjl, bool x_f32, int num_cus,
+hipError_t launch_encode(const EncodeArgs &a, int bits, bool qjl, bool x_f32, bool split, int num_cus,
                          hipStream_t stream);
 // Keys (ka) and values (va, no QJL) of bf16 rows in one launch, no debug outputs.
 hipError_t launch_encode_pair(const EncodeArgs &ka, int kbits, bool kqjl, const EncodeArgs &va, int vbits,
@@ -138,6 +155,9 @@ struct DecodeArgs {
   const void *mk_lut;          // key operand table of the key codebook
   const void *mv_lut;          // value operand table of the value codebook
   const void *sg_lut;          // sign table
+  int k_split, v_split;        // split widths (kSplitWide wide coordinates) of the key / value codebook
+  const void *mk_lut_w;        // split keys: the wide codebook's key operand table
+  const void *mv_lut_w;        // split values: the wide codebook's value operand table
   int norm_vec4;               // t_cap % 4 == 0 and the norm arrays 16-byte aligned (four norms per load)
   float *ws_qslot;
   float *ws_part_o;        // [B*Hkv][n_chunks][g][d]: rotated back (decode kernel) or rotated (chunk kernel)

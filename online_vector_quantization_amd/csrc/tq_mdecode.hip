@@ -53,6 +53,16 @@
 //           coordinates 8 n .. 8 n + 7 (one 8 b'-bit field per token) of the
 //           tokens whose scores it received: the softmax output feeds the B
 //           operand without a transposition.
+//
+// Split widths (SPL: both codebooks put rotated coordinates 0..63 on the
+// (b' + 1)-bit codebook, 64..127 on the b'-bit one, records holding the wide
+// codes first) [cc-newplayer explainer, technical breakdown item 1;
+// intelliparadigm "3-bit" article, §2.1]: the coordinate orders change so that
+// every lane sees both widths at compile-time positions.  Key k-steps 0..3
+// carry wide coordinates 16 kq + 4 s + i and k-steps 4..7 narrow ones
+// 64 + 16 kq + 4 (s - 4) + i; value blocks 0..3 are wide coordinates
+// 4 n + cb and blocks 4..7 narrow ones 64 + 4 n + cb - 4.  Each width has its
+// own key and value tables.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -153,13 +163,49 @@ constexpr int kSignCopies = 8;    // 16-byte entries: 8 lanes x 4 banks per pass
 using PairTab = Striped<8, kPairCopies>;
 using SignTab = Striped<16, kSignCopies>;
 
+// Split widths: record words a lane reads for its 16 wide / 16 narrow key
+// codes (16 w bits from a 16-bit boundary: two words once they may cross one)
+// and for its 4 wide / 4 narrow value codes (4 w bits: two words for w = 3).
+constexpr int split_key_words(int w) { return w > 2 ? 2 : 1; }
+constexpr int split_val_words(int w) { return w == 3 ? 2 : 1; }
+// Words of a lane's key codes per token (kKeyWords) and of its value fields
+// per token (kValWords); split widths: the wide codes' words, then the narrow ones'.
+template <int KB, bool SPL>
+constexpr int kKeyWords = SPL ? split_key_words(KB + 1) + split_key_words(KB) : KB;
+template <int VB, bool SPL>
+constexpr int kValWords = SPL ? split_val_words(VB + 1) + split_val_words(VB) : (VB == 3 ? 2 : 1);
+
+// (hi:lo) = the NW words at w, shifted right by sh bits (sh < 32).
+template <int NW>
+__device__ __forceinline__ void funnel(const uint32_t *w, int sh, uint32_t &lo, uint32_t &hi) {
+  if constexpr (NW == 1) {
+    lo = w[0] >> sh;
+    hi = 0u;
+  } else {
+    lo = __builtin_amdgcn_alignbit(w[1], w[0], sh);
+    hi = w[1] >> sh;
+  }
+}
+
 // One wave's share of a 32-token tile: its records, loaded one tile ahead.
-template <int KB, int VB, bool QJL, bool SC> struct Tile {
-  uint32_t kc[2][KB];          // key code words kq KB .. of token n of each half
+template <int KB, int VB, bool QJL, bool SC, bool SPL> struct Tile {
+  uint32_t kc[2][kKeyWords<KB, SPL>];   // key code words of token n of each half
   uint32_t sg[2];              // sign word kq of token n of each half
   float knu[4], gam[4];        // tokens 4 kq + e of the lane's own half (columns 0..7: the first)
-  uint32_t vf[SC ? 1 : 8][VB == 3 ? 2 : 1];   // value words holding coordinates 8 n .. 8 n + 7 of tokens T(i)
+  uint32_t vf[SC ? 1 : 8][kValWords<VB, SPL>];   // value words holding the lane's coordinates of tokens T(i)
   float vnu[SC ? 1 : 4];       // value norms of the lane's own half's tokens
+};
+
+// Split widths: first record word and bit shift of a lane's key codes (wide:
+// coordinates 16 kq .., narrow: 64 + 16 kq ..) and of its value fields (wide:
+// coordinates 4 n .. 4 n + 3, narrow: 64 + 4 n ..) in a record of
+// split_code_words(b') words.
+template <int B> struct SplitRec {
+  static constexpr int W = B + 1, N = B, CW = split_code_words(B);
+  static constexpr int key_wide_bit(int kq) { return 16 * kq * W; }
+  static constexpr int key_narrow_bit(int kq) { return 64 * W + 16 * kq * N; }
+  static constexpr int val_wide_bit(int n) { return 4 * n * W; }
+  static constexpr int val_narrow_bit(int n) { return 64 * W + 4 * n * N; }
 };
 
 // Token T(i) of the lane's value fields: 4 kq + (i & 3) of half i >> 2.
@@ -168,18 +214,35 @@ template <int KB, int VB, bool QJL, bool SC> struct Tile {
 // token (tiles past seq_len are masked when used), byte offsets are 32-bit
 // on a uniform row base, and the norms come four at a time (the row length
 // is a multiple of 4 and the norm arrays 16-byte aligned on this path).
-template <int KB, int VB, bool QJL, bool SC>
+template <int KB, int VB, bool QJL, bool SC, bool SPL>
 __device__ __forceinline__ void load_tile(const DecodeArgs &a, int64_t row0, int tb, int n, int kq, bool lo_col,
-                                          Tile<KB, VB, QJL, SC> &r) {
-  constexpr int VW = 4 * VB;
+                                          Tile<KB, VB, QJL, SC, SPL> &r) {
+  // words per record
+  constexpr int KW = SPL ? split_code_words(KB) : 4 * KB;
+  constexpr int VW = SPL ? split_code_words(VB) : 4 * VB;
   const int last = static_cast<int>(a.t_cap) - 1;
-  const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k_codes + row0 * (4 * KB));
+  const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k_codes + row0 * KW);
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const uint32_t tk = static_cast<uint32_t>(min(tb + 16 * hf + n, last));
-    const uint32_t ko = (tk * (4 * KB) + kq * KB) * 4u;
+    if constexpr (SPL) {
+      // the lane's 16 W wide bits lie within words w0, w0 + 1 (the second
+      // only read when they can reach it), its 16 N narrow bits likewise;
+      // every word read lies inside the record
+      using R = SplitRec<KB>;
+      constexpr int NWW = split_key_words(R::W), NWN = split_key_words(R::N);
+      const uint32_t kw = static_cast<uint32_t>(R::key_wide_bit(kq) >> 5);
+      const uint32_t kn = static_cast<uint32_t>(R::key_narrow_bit(kq) >> 5);
+      const unsigned char *rec = kbase + tk * (KW * 4u);
 #pragma unroll
-    for (int w = 0; w < KB; ++w) r.kc[hf][w] = *reinterpret_cast<const uint32_t *>(kbase + 4 * w + ko);
+      for (int w = 0; w < NWW; ++w) r.kc[hf][w] = *reinterpret_cast<const uint32_t *>(rec + 4 * (kw + w));
+#pragma unroll
+      for (int w = 0; w < NWN; ++w) r.kc[hf][NWW + w] = *reinterpret_cast<const uint32_t *>(rec + 4 * (kn + w));
+    } else {
+      const uint32_t ko = (tk * (4 * KB) + kq * KB) * 4u;
+#pragma unroll
+      for (int w = 0; w < KB; ++w) r.kc[hf][w] = *reinterpret_cast<const uint32_t *>(kbase + 4 * w + ko);
+    }
     if constexpr (QJL)
       r.sg[hf] = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const unsigned char *>(a.k_signs + row0 * 4) +
                                                      (tk * 4u + kq) * 4u);
@@ -195,13 +258,30 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, int64_t row0, int
   }
   if constexpr (!SC) {
     const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v_codes + row0 * VW);
-    const int w0 = (8 * n * VB) >> 5;   // first word of the lane's value field
+    if constexpr (SPL) {
+      // wide field: 4 W bits from word vw, narrow: 4 N bits from word vn; a
+      // 3-bit field may straddle into the next word (read when inside the record)
+      using R = SplitRec<VB>;
+      constexpr int NWW = split_val_words(R::W), NWN = split_val_words(R::N);
+      const int vw = R::val_wide_bit(n) >> 5, vn = R::val_narrow_bit(n) >> 5;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t tv = static_cast<uint32_t>(min(tb + 16 * (i >> 2) + 4 * kq + (i & 3), last));
-      const uint32_t vo = (tv * VW + w0) * 4u;
-      r.vf[i][0] = *reinterpret_cast<const uint32_t *>(vbase + vo);
-      if constexpr (VB == 3) r.vf[i][1] = (w0 + 1 < VW) ? *reinterpret_cast<const uint32_t *>(vbase + vo + 4) : 0u;
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t tv = static_cast<uint32_t>(min(tb + 16 * (i >> 2) + 4 * kq + (i & 3), last));
+        const unsigned char *rec = vbase + tv * (VW * 4u);
+        r.vf[i][0] = *reinterpret_cast<const uint32_t *>(rec + 4 * vw);
+        if constexpr (NWW == 2) r.vf[i][1] = *reinterpret_cast<const uint32_t *>(rec + 4 * vw + 4);
+        r.vf[i][NWW] = *reinterpret_cast<const uint32_t *>(rec + 4 * vn);
+        if constexpr (NWN == 2) r.vf[i][NWW + 1] = (vn + 1 < VW) ? *reinterpret_cast<const uint32_t *>(rec + 4 * vn + 4) : 0u;
+      }
+    } else {
+      const int w0 = (8 * n * VB) >> 5;   // first word of the lane's value field
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t tv = static_cast<uint32_t>(min(tb + 16 * (i >> 2) + 4 * kq + (i & 3), last));
+        const uint32_t vo = (tv * VW + w0) * 4u;
+        r.vf[i][0] = *reinterpret_cast<const uint32_t *>(vbase + vo);
+        if constexpr (VB == 3) r.vf[i][1] = (w0 + 1 < VW) ? *reinterpret_cast<const uint32_t *>(vbase + vo + 4) : 0u;
+      }
     }
     const float4 vv = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(a.v_norms + row0) + t4);
     r.vnu[0] = vv.x; r.vnu[1] = vv.y; r.vnu[2] = vv.z; r.vnu[3] = vv.w;
@@ -225,13 +305,28 @@ template <> struct EvenMask<2> { static constexpr uint32_t v = 0x3333u; };
 template <> struct EvenMask<3> { static constexpr uint32_t v = 0x1C71C7u; };
 template <> struct EvenMask<4> { static constexpr uint32_t v = 0x0F0F0F0Fu; };
 
-template <int KB, int VB, bool QJL, bool SC>
+// Bits [bit, bit + WIDTH) of the 64-bit value (hi:lo); bit and WIDTH known at
+// compile time after unrolling.
+template <int WIDTH>
+__device__ __forceinline__ uint32_t bits_at(uint32_t lo, uint32_t hi, int bit) {
+  constexpr uint32_t kMask = (1u << WIDTH) - 1u;
+  if (bit >= 32) return (hi >> (bit - 32)) & kMask;
+  if (bit + WIDTH <= 32) return (lo >> bit) & kMask;
+  return __builtin_amdgcn_alignbit(hi, lo, bit) & kMask;
+}
+
+template <int KB, int VB, bool QJL, bool SC, bool SPL>
 __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   constexpr int kKeyEntries = 1 << (2 * KB);
   constexpr int kValEntries = SC ? 1 : 1 << (2 * VB);
+  // split widths: the wide codebooks' tables (b' + 1 bits)
+  constexpr int kKeyEntriesW = SPL ? 1 << (2 * KB + 2) : 1;
+  constexpr int kValEntriesW = (SPL && !SC) ? 1 << (2 * VB + 2) : 1;
   struct Smem {
     alignas(16) unsigned char ktab[kKeyEntries * PairTab::kRow];
     alignas(16) unsigned char vtab[kValEntries * PairTab::kRow];
+    alignas(16) unsigned char ktab_w[kKeyEntriesW * PairTab::kRow];
+    alignas(16) unsigned char vtab_w[kValEntriesW * PairTab::kRow];
     alignas(16) unsigned char stab[QJL ? 256 * SignTab::kRow : 16];
     union {
       struct {
@@ -277,24 +372,26 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
 
   // The wave's first tile is requested before the prologue, whose work then
   // hides its memory latency.
-  Tile<KB, VB, QJL, SC> ta{};
+  Tile<KB, VB, QJL, SC, SPL> ta{};
   int t0 = t_begin + wave * kTile;
-  if (t0 < t_end) load_tile<KB, VB, QJL, SC>(a, row0, t0, n, kq, lo_col, ta);
+  if (t0 < t_end) load_tile<KB, VB, QJL, SC, SPL>(a, row0, t0, n, kq, lo_col, ta);
 
   // ------------------------------------------------------------ prologue
   // Striped copies of the codebooks' tables (key code pairs -> fp16 (hi, lo)
   // of 256 c per code, pairs of tokens' value codes -> bf16 (hi, lo) of c per
   // token, sign bytes -> eight fp16 +-1).
   {
-    const uint2 *kt = reinterpret_cast<const uint2 *>(a.mk_lut);
-    for (int i = tid; i < kKeyEntries * PairTab::kCopies; i += kThreads)
-      *reinterpret_cast<uint2 *>(sm.ktab + (i / PairTab::kCopies) * PairTab::kRow + (i % PairTab::kCopies) * 8) =
-          kt[i / PairTab::kCopies];
+    auto fill_pairs = [&](unsigned char *dst, const void *src, int entries) {
+      const uint2 *t = reinterpret_cast<const uint2 *>(src);
+      for (int i = tid; i < entries * PairTab::kCopies; i += kThreads)
+        *reinterpret_cast<uint2 *>(dst + (i / PairTab::kCopies) * PairTab::kRow + (i % PairTab::kCopies) * 8) =
+            t[i / PairTab::kCopies];
+    };
+    fill_pairs(sm.ktab, a.mk_lut, kKeyEntries);
+    if constexpr (SPL) fill_pairs(sm.ktab_w, a.mk_lut_w, kKeyEntriesW);
     if constexpr (!SC) {
-      const uint2 *vt = reinterpret_cast<const uint2 *>(a.mv_lut);
-      for (int i = tid; i < kValEntries * PairTab::kCopies; i += kThreads)
-        *reinterpret_cast<uint2 *>(sm.vtab + (i / PairTab::kCopies) * PairTab::kRow + (i % PairTab::kCopies) * 8) =
-            vt[i / PairTab::kCopies];
+      fill_pairs(sm.vtab, a.mv_lut, kValEntries);
+      if constexpr (SPL) fill_pairs(sm.vtab_w, a.mv_lut_w, kValEntriesW);
     }
     if constexpr (QJL) {
       const uint4 *st = reinterpret_cast<const uint4 *>(a.sg_lut);
@@ -379,8 +476,9 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   // The scores' B operands, column n: the query part of head n % 8 times
   // 2^fexp (fp16 hi part in columns 0..7, lo part in 8..15, zero for columns
   // past g).  Key product, k-step s: K-element pair i carries coordinate
-  // 32 kq + 4 s + i twice (the key operand holds its (hi, lo) parts); sign
-  // product, k-step s: coordinates 32 kq + 8 s .. + 7 once.  The products
+  // 32 kq + 4 s + i (split widths: 64 (s / 4) + 16 kq + 4 (s % 4) + i) twice
+  // (the key operand holds its (hi, lo) parts); sign product, k-step s:
+  // QJL coordinates 32 kq + 8 s .. + 7 once.  The products
   // come out scaled by 2^fexp_q * kKeyScale (key term) and 2^fexp_s (sign
   // term): undone per lane below.
   f16x8 qop[8], sop[QJL ? 4 : 1];
@@ -390,7 +488,8 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
     uint32_t wq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float x = ldexpf(sm.u.pro.qt[hcol][32 * kq + 4 * s + i], eq);
+      const int c = SPL ? 64 * (s >> 2) + 16 * kq + 4 * (s & 3) + i : 32 * kq + 4 * s + i;
+      const float x = ldexpf(sm.u.pro.qt[hcol][c], eq);
       wq[i] = split_f16(x, x, lo_col);
     }
     qop[s] = as_f16x8(wq[0], wq[1], wq[2], wq[3]);
@@ -420,9 +519,15 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   for (int cb = 0; cb < 8; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint32_t lane_p = 8u * (n % PairTab::kCopies);   // this lane's copy in the pair tables
   const uint32_t lane_s = 16u * (n % SignTab::kCopies);  // and in the sign table
+  // split widths: bit offsets of the lane's key codes and value fields within
+  // the first word load_tile reads for them
+  const int sh_kw = SPL ? SplitRec<KB>::key_wide_bit(kq) & 31 : 0;
+  const int sh_kn = SPL ? SplitRec<KB>::key_narrow_bit(kq) & 31 : 0;
+  const int sh_vw = (SPL && !SC) ? SplitRec<VB>::val_wide_bit(n) & 31 : 0;
+  const int sh_vn = (SPL && !SC) ? SplitRec<VB>::val_narrow_bit(n) & 31 : 0;
 
   // One tile: scores (key and sign products), online softmax, value product.
-  auto compute = [&](const Tile<KB, VB, QJL, SC> &cur, int tb) {
+  auto compute = [&](const Tile<KB, VB, QJL, SC, SPL> &cur, int tb) {
     const bool full = tb + kTile <= t_end;
     // ---- scores C[token 4 kq + e][column n] of both halves.  K-element
     // pair i of k-step s is (hi, lo) of coordinate 32 kq + 4 s + i (keys), or
@@ -432,24 +537,40 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
     for (int hf = 0; hf < 2; ++hf) {
       sacc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
       tacc[hf] = sacc[hf];
+      // split widths: the lane's 16 wide codes (bits of kw1:kw0) and 16
+      // narrow codes (kn1:kn0), shifted to bit 0
+      uint32_t kw0 = 0, kw1 = 0, kn0 = 0, kn1 = 0;
+      if constexpr (SPL) {
+        constexpr int NWW = split_key_words(KB + 1);
+        funnel<NWW>(&cur.kc[hf][0], sh_kw, kw0, kw1);
+        funnel<split_key_words(KB)>(&cur.kc[hf][NWW], sh_kn, kn0, kn1);
+      }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         uint32_t ka[2];
+        const bool wide = SPL && s < 4;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          // pair q = 2 s + p: bits [2 KB q, 2 KB q + 2 KB) of the lane's codes
-          constexpr int kMask = (1 << (2 * KB)) - 1;
-          const int bit = 2 * KB * (2 * s + p), w = bit >> 5, sh = bit & 31;
           uint32_t idx;
-          if (sh + 2 * KB <= 32) {
-            idx = (cur.kc[hf][w] >> sh) & kMask;
+          if constexpr (SPL) {
+            // pair q of the step's width: bits [2 w q, 2 w q + 2 w)
+            const int q = 2 * (s & 3) + p;
+            idx = wide ? bits_at<2 * KB + 2>(kw0, kw1, (2 * KB + 2) * q) : bits_at<2 * KB>(kn0, kn1, 2 * KB * q);
           } else {
-            idx = __builtin_amdgcn_alignbit(cur.kc[hf][w + 1], cur.kc[hf][w], sh) & kMask;
+            // pair q = 2 s + p: bits [2 KB q, 2 KB q + 2 KB) of the lane's codes
+            constexpr int kMask = (1 << (2 * KB)) - 1;
+            const int bit = 2 * KB * (2 * s + p), w = bit >> 5, sh = bit & 31;
+            if (sh + 2 * KB <= 32) {
+              idx = (cur.kc[hf][w] >> sh) & kMask;
+            } else {
+              idx = __builtin_amdgcn_alignbit(cur.kc[hf][w + 1], cur.kc[hf][w], sh) & kMask;
+            }
           }
           ka[p] = (idx << PairTab::kShift) + lane_p;
         }
-        const uint2 e0 = *reinterpret_cast<const uint2 *>(sm.ktab + ka[0]);
-        const uint2 e1 = *reinterpret_cast<const uint2 *>(sm.ktab + ka[1]);
+        const unsigned char *kt = wide ? sm.ktab_w : sm.ktab;
+        const uint2 e0 = *reinterpret_cast<const uint2 *>(kt + ka[0]);
+        const uint2 e1 = *reinterpret_cast<const uint2 *>(kt + ka[1]);
         sacc[hf] = mfma_f16(as_f16x8(e0.x, e0.y, e1.x, e1.y), qop[s], sacc[hf]);
       }
       if constexpr (QJL) {
@@ -521,43 +642,86 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
         pb[hf] = as_bf16x8(__builtin_amdgcn_perm(p01, p01, 0x01000100u), __builtin_amdgcn_perm(p01, p01, 0x03020302u),
                            __builtin_amdgcn_perm(p23, p23, 0x01000100u), __builtin_amdgcn_perm(p23, p23, 0x03020302u));
       }
-      // ---- value sum: block cb, row n = coordinate 8 n + cb; K-element pair
-      // i = (hi, lo) of token 4 kq + i of the half
+      // ---- value sum: block cb, row n = coordinate 8 n + cb (split widths:
+      // 4 n + cb wide, 64 + 4 n + cb - 4 narrow); K-element pair i = (hi, lo)
+      // of token 4 kq + i of the half
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        uint32_t E[2], O[2];
+        if constexpr (SPL) {
+          // per width: the 4 codes of the lane's coordinates of tokens
+          // (2 pp, 2 pp + 1), paired per coordinate as in the uniform case
+          constexpr int W = VB + 1, N = VB, NWW = split_val_words(W), NWN = split_val_words(N);
+          constexpr uint32_t MW = EvenMask<W>::v & ((1u << (4 * W)) - 1u);
+          constexpr uint32_t MN = EvenMask<N>::v & ((1u << (4 * N)) - 1u);
+          uint32_t EW[2], OW[2], EN[2], ON[2];
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          // tokens (2 pp, 2 pp + 1) of the half: the pair index of every
-          // coordinate, even coordinates in E, odd ones in O
-          constexpr uint32_t M = EvenMask<VB>::v;
-          const uint32_t f0 = value_field<VB>(cur.vf[4 * hf + 2 * pp], n);
-          const uint32_t f1 = value_field<VB>(cur.vf[4 * hf + 2 * pp + 1], n);
-          E[pp] = (f0 & M) | ((f1 & M) << VB);
-          O[pp] = ((f0 >> VB) & M) | (f1 & (M << VB));
-        }
+          for (int pp = 0; pp < 2; ++pp) {
+            const uint32_t *v0 = cur.vf[4 * hf + 2 * pp];
+            const uint32_t *v1 = cur.vf[4 * hf + 2 * pp + 1];
+            uint32_t w0, w1, n0, n1, hi;
+            funnel<NWW>(v0, sh_vw, w0, hi);
+            funnel<NWW>(v1, sh_vw, w1, hi);
+            funnel<NWN>(v0 + NWW, sh_vn, n0, hi);
+            funnel<NWN>(v1 + NWW, sh_vn, n1, hi);
+            w0 &= (1u << (4 * W)) - 1u;
+            w1 &= (1u << (4 * W)) - 1u;
+            n0 &= (1u << (4 * N)) - 1u;
+            n1 &= (1u << (4 * N)) - 1u;
+            EW[pp] = (w0 & MW) | ((w1 & MW) << W);
+            OW[pp] = ((w0 >> W) & MW) | (w1 & (MW << W));
+            EN[pp] = (n0 & MN) | ((n1 & MN) << N);
+            ON[pp] = ((n0 >> N) & MN) | (n1 & (MN << N));
+          }
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          constexpr uint32_t kMask = (1u << (2 * VB)) - 1u;
-          const int sh = 2 * VB * (cb >> 1);
-          const uint32_t i0 = (((cb & 1) ? O[0] : E[0]) >> sh) & kMask;
-          const uint32_t i1 = (((cb & 1) ? O[1] : E[1]) >> sh) & kMask;
-          const uint2 e0 = *reinterpret_cast<const uint2 *>(sm.vtab + (i0 << PairTab::kShift) + lane_p);
-          const uint2 e1 = *reinterpret_cast<const uint2 *>(sm.vtab + (i1 << PairTab::kShift) + lane_p);
-          oacc[cb] = mfma(as_bf16x8(e0.x, e0.y, e1.x, e1.y), pb[hf], oacc[cb]);
+          for (int cb = 0; cb < 8; ++cb) {
+            const bool wide = cb < 4;
+            const int c = cb & 3;
+            const int width = wide ? W : N;
+            const uint32_t mask = (1u << (2 * width)) - 1u;
+            const int sh = 2 * width * (c >> 1);
+            const uint32_t s0 = wide ? ((c & 1) ? OW[0] : EW[0]) : ((c & 1) ? ON[0] : EN[0]);
+            const uint32_t s1 = wide ? ((c & 1) ? OW[1] : EW[1]) : ((c & 1) ? ON[1] : EN[1]);
+            const uint32_t i0 = (s0 >> sh) & mask, i1 = (s1 >> sh) & mask;
+            const unsigned char *vt = wide ? sm.vtab_w : sm.vtab;
+            const uint2 e0 = *reinterpret_cast<const uint2 *>(vt + (i0 << PairTab::kShift) + lane_p);
+            const uint2 e1 = *reinterpret_cast<const uint2 *>(vt + (i1 << PairTab::kShift) + lane_p);
+            oacc[cb] = mfma(as_bf16x8(e0.x, e0.y, e1.x, e1.y), pb[hf], oacc[cb]);
+          }
+        } else {
+          uint32_t E[2], O[2];
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            // tokens (2 pp, 2 pp + 1) of the half: the pair index of every
+            // coordinate, even coordinates in E, odd ones in O
+            constexpr uint32_t M = EvenMask<VB>::v;
+            const uint32_t f0 = value_field<VB>(cur.vf[4 * hf + 2 * pp], n);
+            const uint32_t f1 = value_field<VB>(cur.vf[4 * hf + 2 * pp + 1], n);
+            E[pp] = (f0 & M) | ((f1 & M) << VB);
+            O[pp] = ((f0 >> VB) & M) | (f1 & (M << VB));
+          }
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb) {
+            constexpr uint32_t kMask = (1u << (2 * VB)) - 1u;
+            const int sh = 2 * VB * (cb >> 1);
+            const uint32_t i0 = (((cb & 1) ? O[0] : E[0]) >> sh) & kMask;
+            const uint32_t i1 = (((cb & 1) ? O[1] : E[1]) >> sh) & kMask;
+            const uint2 e0 = *reinterpret_cast<const uint2 *>(sm.vtab + (i0 << PairTab::kShift) + lane_p);
+            const uint2 e1 = *reinterpret_cast<const uint2 *>(sm.vtab + (i1 << PairTab::kShift) + lane_p);
+            oacc[cb] = mfma(as_bf16x8(e0.x, e0.y, e1.x, e1.y), pb[hf], oacc[cb]);
+          }
         }
       }
     }
   };
 
   constexpr int kStride = kWaves * kTile;
-  Tile<KB, VB, QJL, SC> tn{};
+  Tile<KB, VB, QJL, SC, SPL> tn{};
   // two tile buffers in turn: one is computed while the next is loaded
   for (; t0 < t_end; t0 += 2 * kStride) {
-    if (t0 + kStride < t_end) load_tile<KB, VB, QJL, SC>(a, row0, t0 + kStride, n, kq, lo_col, tn);
+    if (t0 + kStride < t_end) load_tile<KB, VB, QJL, SC, SPL>(a, row0, t0 + kStride, n, kq, lo_col, tn);
     compute(ta, t0);
     if (t0 + kStride >= t_end) break;
-    if (t0 + 2 * kStride < t_end) load_tile<KB, VB, QJL, SC>(a, row0, t0 + 2 * kStride, n, kq, lo_col, ta);
+    if (t0 + 2 * kStride < t_end) load_tile<KB, VB, QJL, SC, SPL>(a, row0, t0 + 2 * kStride, n, kq, lo_col, ta);
     compute(tn, t0 + kStride);
   }
 
@@ -587,13 +751,15 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.ml[w][hcol][0]);
     const float fw = (m_run == -INFINITY) ? 0.f : exp2f(m_run - mx);
-    // rows 4 kq + e of block cb are coordinates 8 (4 kq + e) + cb
+    // rows 4 kq + e of block cb are coordinates 8 (4 kq + e) + cb (split
+    // widths: 64 (cb / 4) + 4 (4 kq + e) + cb % 4)
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float v = (oacc[cb][e] + swap8(oacc[cb][e])) * fw;
-        if (!lo_col) sm.u.epi.o[wave][kq][hcol][8 * e + cb] = v;   // coordinate 32 kq + 8 e + cb
+        const int c = SPL ? 64 * (cb >> 2) + 16 * kq + 4 * e + (cb & 3) : 32 * kq + 8 * e + cb;
+        if (!lo_col) sm.u.epi.o[wave][c >> 5][hcol][c & 31] = v;
       }
   }
   __syncthreads();
@@ -671,26 +837,30 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   }
 }
 
-template <int KB, bool QJL, bool SC>
+template <int KB, bool QJL, bool SC, bool SPL>
 hipError_t launch_v(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
   if constexpr (SC) {
     // scores only: no value table (the VB argument is unused)
-    hipLaunchKernelGGL((mdecode_kernel<KB, 4, QJL, true>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mdecode_kernel<KB, 4, QJL, true, SPL>), grid, dim3(kThreads), 0, stream, a);
   } else {
     switch (a.v_bits) {
 #define TQ_V(VV) \
-  case VV: hipLaunchKernelGGL((mdecode_kernel<KB, VV, QJL, false>), grid, dim3(kThreads), 0, stream, a); break;
-      TQ_V(1) TQ_V(2) TQ_V(3) TQ_V(4)
+  case VV: hipLaunchKernelGGL((mdecode_kernel<KB, VV, QJL, false, SPL>), grid, dim3(kThreads), 0, stream, a); break;
+      TQ_V(1) TQ_V(2) TQ_V(3)
 #undef TQ_V
+      case 4:
+        if constexpr (SPL) return hipErrorInvalidValue;   // split widths: b' + 1 <= 4
+        else hipLaunchKernelGGL((mdecode_kernel<KB, 4, QJL, false, false>), grid, dim3(kThreads), 0, stream, a);
+        break;
       default: return hipErrorInvalidValue;
     }
   }
   return hipGetLastError();
 }
 
-template <int KB, bool SC>
+template <int KB, bool SC, bool SPL>
 hipError_t launch_k(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
-  return a.qjl_m > 0 ? launch_v<KB, true, SC>(a, grid, stream) : launch_v<KB, false, SC>(a, grid, stream);
+  return a.qjl_m > 0 ? launch_v<KB, true, SC, SPL>(a, grid, stream) : launch_v<KB, false, SC, SPL>(a, grid, stream);
 }
 
 }  // namespace
@@ -699,14 +869,24 @@ hipError_t launch_mdecode_main(const DecodeArgs &a, bool scores_only, hipStream_
   const int g = a.n_q_heads / a.n_kv_heads;
   if (!mdecode_applies(a) || a.n_chunks > kMaxDecodeChunks || g < 1 || g > 8 || a.n_kv_heads > 65535 ||
       a.mk_lut == nullptr || a.rot_k_t == nullptr || (a.qjl_m > 0 && (a.qjl_rot_t == nullptr || a.sg_lut == nullptr)) ||
-      (!scores_only && a.mv_lut == nullptr))
+      (!scores_only && a.mv_lut == nullptr) || (a.k_split && a.mk_lut_w == nullptr) ||
+      (!scores_only && (a.v_split != a.k_split || (a.v_split && a.mv_lut_w == nullptr))))
     return hipErrorInvalidValue;
   const dim3 grid(a.n_chunks, a.n_kv_heads, a.batch);
+  if (a.k_split) {
+    // split widths (both codebooks): b' + 1 <= 4
+    switch (a.k_bits) {
+      case 1: return scores_only ? launch_k<1, true, true>(a, grid, stream) : launch_k<1, false, true>(a, grid, stream);
+      case 2: return scores_only ? launch_k<2, true, true>(a, grid, stream) : launch_k<2, false, true>(a, grid, stream);
+      case 3: return scores_only ? launch_k<3, true, true>(a, grid, stream) : launch_k<3, false, true>(a, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.k_bits) {
-    case 1: return scores_only ? launch_k<1, true>(a, grid, stream) : launch_k<1, false>(a, grid, stream);
-    case 2: return scores_only ? launch_k<2, true>(a, grid, stream) : launch_k<2, false>(a, grid, stream);
-    case 3: return scores_only ? launch_k<3, true>(a, grid, stream) : launch_k<3, false>(a, grid, stream);
-    case 4: return scores_only ? launch_k<4, true>(a, grid, stream) : launch_k<4, false>(a, grid, stream);
+    case 1: return scores_only ? launch_k<1, true, false>(a, grid, stream) : launch_k<1, false, false>(a, grid, stream);
+    case 2: return scores_only ? launch_k<2, true, false>(a, grid, stream) : launch_k<2, false, false>(a, grid, stream);
+    case 3: return scores_only ? launch_k<3, true, false>(a, grid, stream) : launch_k<3, false, false>(a, grid, stream);
+    case 4: return scores_only ? launch_k<4, true, false>(a, grid, stream) : launch_k<4, false, false>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -200,7 +200,7 @@ float bf16_bits_to_float(uint16_t b) {
   return f;
 }
 
-bool build_host_tables(int d, int bits, int m, uint64_t rot_seed, uint64_t qjl_seed,
+bool build_host_tables(int d, int bits, int n_wide, int m, uint64_t rot_seed, uint64_t qjl_seed,
                        HostTables *out, std::string *err) {
   if (d < 2 || d > 4096) {
     *err = "head_dim must be in [2, 4096]";
@@ -214,13 +214,23 @@ bool build_host_tables(int d, int bits, int m, uint64_t rot_seed, uint64_t qjl_s
     *err = "qjl_dim must be 0 or a positive multiple of 32 (<= 4096)";
     return false;
   }
+  if (n_wide < 0 || n_wide > d || (n_wide > 0 && bits > 3)) {
+    *err = "wide_coords must be in [0, head_dim], and mse_bits <= 3 when it is positive";
+    return false;
+  }
   HostTables h;
   h.d = d;
   h.bits = bits;
   h.m = m;
   h.levels = 1 << bits;
+  h.n_wide = n_wide;
   int iters = 0;
   lloyd_max_sphere(d, bits, &h.centroids64, &h.thresholds64, &iters);
+  // [cc-newplayer explainer, technical breakdown item 1] and [intelliparadigm
+  // "3-bit" article, §2.1 and §5.1]: fractional average widths; every rotated
+  // coordinate has the same law, so the wide part takes the plain
+  // (bits + 1)-bit Lloyd-Max codebook of that law.
+  if (n_wide > 0) lloyd_max_sphere(d, bits + 1, &h.wide_centroids64, &h.wide_thresholds64, &iters);
   h.rotation64.resize(static_cast<size_t>(d) * d);
   haar_orthogonal(d, rot_seed, h.rotation64.data());
   if (m > 0) {
@@ -235,6 +245,8 @@ bool build_host_tables(int d, int bits, int m, uint64_t rot_seed, uint64_t qjl_s
   to_f32(h.thresholds64, &h.thresholds);
   to_f32(h.rotation64, &h.rotation);
   to_f32(h.qjl64, &h.qjl);
+  to_f32(h.wide_centroids64, &h.wide_centroids);
+  to_f32(h.wide_thresholds64, &h.wide_thresholds);
   *out = std::move(h);
   return true;
 }

@@ -17,17 +17,22 @@ ROT_SEED, QJL_SEED = 0, 1
 _books = {}
 
 
-def oracle_book(bits: int, m: int, d: int = 128):
-    key = (bits, m, d)
+def oracle_book(bits: int, m: int, d: int = 128, wide: int = 0):
+    """The oracle's decode book; wide > 0: split widths (the first `wide`
+    rotated coordinates on the (bits + 1)-bit codebook)."""
+    key = (bits, m, d, wide)
     if key not in _books:
-        c, t = O.build_codebook(d, bits)
-        _books[key] = {"bits": bits, "centroids": c, "thresholds": t, "Pi": O.haar_rotation(d, ROT_SEED),
-                       "S": O.qjl_matrix(m, d, QJL_SEED) if m else None}
+        extra = {"Pi": O.haar_rotation(d, ROT_SEED), "S": O.qjl_matrix(m, d, QJL_SEED) if m else None}
+        if wide:
+            _books[key] = dict(O.build_split_book(d, bits, wide), **extra)
+        else:
+            c, t = O.build_codebook(d, bits)
+            _books[key] = dict({"bits": bits, "centroids": c, "thresholds": t}, **extra)
     return _books[key]
 
 
-def gpu_book(bits: int, m: int) -> T.Codebook:
-    return T.Codebook(128, bits, m, ROT_SEED, QJL_SEED, device=0)
+def gpu_book(bits: int, m: int, wide: int = 0) -> T.Codebook:
+    return T.Codebook(128, bits, m, ROT_SEED, QJL_SEED, device=0, wide_coords=wide)
 
 
 def to_device(x: np.ndarray, dtype: str) -> torch.Tensor:
@@ -66,14 +71,17 @@ def encode_gpu(cb: T.Codebook, x_dev: torch.Tensor, rows: int = None, dst_row=No
     return out
 
 
-def check_encode(x_host: np.ndarray, got: dict, bits: int, m: int, rows=None, tol=1e-4):
+def check_encode(x_host: np.ndarray, got: dict, bits: int, m: int, rows=None, tol=1e-4, wide: int = 0):
     """Parity of one encode against the oracle; returns the near-boundary flip count.
 
-    rows[i] is the cache row of input row i (default i).
+    rows[i] is the cache row of input row i (default i); wide > 0: split widths.
     """
-    bk = oracle_book(bits, m)
+    bk = oracle_book(bits, m, wide=wide)
     rows = np.arange(x_host.shape[0]) if rows is None else rows
-    ref = O.encode(x_host.astype(np.float64), bk["Pi"], bk["centroids"], bk["thresholds"], bk["S"])
+    if wide:
+        ref = O.encode_split(x_host.astype(np.float64), bk["Pi"], bk, bk["S"])
+    else:
+        ref = O.encode(x_host.astype(np.float64), bk["Pi"], bk["centroids"], bk["thresholds"], bk["S"])
     y = got["y"]
     # rotated values: per vector ||dy||_inf <= tol * ||y||_inf
     scale = np.abs(ref["y"]).max(axis=1)
@@ -83,11 +91,19 @@ def check_encode(x_host: np.ndarray, got: dict, bits: int, m: int, rows=None, to
     nu = got["norms"][rows].astype(np.float64)
     assert np.all(np.abs(nu - ref["nu"]) <= tol * ref["nu"] + 1e-30), "norm mismatch"
     # codes: the oracle quantizes the GPU's fp32 rotated values -> bit-exact
-    idx = O.quantize(y, bk["thresholds"])
-    np.testing.assert_array_equal(got["codes"][rows], O.pack_bits(idx, bits))
+    if wide:
+        idx = O.quantize_split(y, bk)
+        np.testing.assert_array_equal(got["codes"][rows], O.pack_bits_widths(idx, O.split_widths(128, bits, wide)))
+    else:
+        idx = O.quantize(y, bk["thresholds"])
+        np.testing.assert_array_equal(got["codes"][rows], O.pack_bits(idx, bits))
     flips = int(np.sum(idx != ref["idx"]))
     if m:
-        r, gamma = O.residual_from_rotated(y, idx, bk["centroids"])
+        if wide:
+            r = y.astype(np.float64) - O.dequant_split(idx, bk)
+            gamma = np.sqrt(np.sum(r * r, axis=1))
+        else:
+            r, gamma = O.residual_from_rotated(y, idx, bk["centroids"])
         assert np.all(np.abs(got["res_norms"][rows] - gamma) <= tol * gamma + 1e-30), "residual norm mismatch"
         p_ref = r @ bk["S"].T
         pscale = np.abs(p_ref).max(axis=1)
@@ -119,7 +135,7 @@ def rne_bf16(x: np.ndarray) -> np.ndarray:
     return synth.bf16_to_f32(synth.bf16_bits(x.astype(np.float32)))
 
 
-def check_decode(kcb, vcb, q_dev, kc, vc, seq_len, kbits, vbits, m, score_tol=1e-4, out_tol=2e-3):
+def check_decode(kcb, vcb, q_dev, kc, vc, seq_len, kbits, vbits, m, score_tol=1e-4, out_tol=2e-3, wide=0):
     B, Hq, _ = q_dev.shape
     t_cap = kc.t_cap
     sl = torch.tensor(seq_len, dtype=torch.int32, device=DEV)
@@ -133,7 +149,7 @@ def check_decode(kcb, vcb, q_dev, kc, vc, seq_len, kbits, vbits, m, score_tol=1e
     np.testing.assert_array_equal(o32.view(np.uint32), out32b.cpu().numpy().view(np.uint32))
     # bf16 output is the RNE rounding of the fp32 output
     np.testing.assert_array_equal(out16.float().cpu().numpy(), rne_bf16(o32))
-    kb, vb = oracle_book(kbits, m), oracle_book(vbits, 0)
+    kb, vb = oracle_book(kbits, m, wide=wide), oracle_book(vbits, 0, wide=wide)
     q_host = q_dev.float().cpu().numpy().astype(np.float64)
     seq_c = [min(max(int(s), 0), t_cap) for s in seq_len]
     ref_out, ref_sc = O.decode_attention(q_host, cache_to_host(kc), cache_to_host(vc), seq_c, kb, vb,
@@ -166,11 +182,11 @@ def oracle_logits(q_host, kc_host, seq_c, kb, g, scale=None):
         if Tb == 0:
             continue
         for hk in range(Hq // g):
-            idx = O.unpack_bits(kc_host["codes"][b, hk, :Tb], d, kb["bits"])
+            idx = O.book_codes(kb, kc_host["codes"][b, hk, :Tb], d)
             z = O.unpack_bits(kc_host["signs"][b, hk, :Tb], m, 1).astype(bool) if m else None
             gam = kc_host["res_norms"][b, hk, :Tb] if m else None
             for j in range(g):
-                out[b, hk * g + j, :Tb] = O.decode_scores(q_host[b, hk * g + j], kb["Pi"], kb["centroids"], kb["S"],
+                out[b, hk * g + j, :Tb] = O.decode_scores(q_host[b, hk * g + j], kb["Pi"], O.book_table(kb), kb["S"],
                                                           idx, kc_host["norms"][b, hk, :Tb], gam, z, scale)
     return out
 

@@ -17,19 +17,17 @@ def bench():
     return mod
 
 
-def test_alu_peak_from_unit_counts(bench):
-    # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one fp32 FMA per lane and cycle
-    assert bench.ALU_PEAK_T_FMA == pytest.approx(256 * 4 * 16 * 2.4e9 / 1e12)
-
-
-def test_decode_alu_view(bench):
-    # the 8B layer: 32 q heads x 32768 tokens, 384 multiply-adds each, in 31 us
-    v = bench.decode_alu_view(32 * 32768, 128, 0.031)
-    assert v["algorithmic_fma_per_launch"] == 32 * 32768 * 384
-    assert v["achieved"] == pytest.approx(32 * 32768 * 384 / 31e-6 / 1e12, rel=1e-3)
-    assert v["frac"] == pytest.approx(v["achieved"] / bench.ALU_PEAK_T_FMA, rel=1e-3)
-    # MSE-only keys have no sign term: 256 per (token, q head)
-    assert bench.decode_alu_view(10, 0, 1.0)["algorithmic_fma_per_launch"] == 2560
+def test_decode_mfma_view(bench):
+    # the 8B layer: 8 kv heads x 32768 tokens, g = 4, QJL keys, in 31 us.
+    # Issued: 20 v_mfma_f32_16x16x32 (16384 flops) per 16 tokens of a kv head;
+    # algorithmic: 2 (d + m + d) flops per (token, q head).
+    v = bench.decode_mfma_view(8 * 32768, 4, 128, 0.031)
+    assert v["flops_per_launch_issued"] == 8 * 32768 * 20 * 16384 / 16
+    assert v["flops_per_launch_algorithmic"] == 8 * 32768 * 4 * 768
+    assert v["achieved_issued"] == pytest.approx(8 * 32768 * 20480 / 31e-6 / 1e12, rel=1e-3)
+    assert v["frac_issued"] == pytest.approx(v["achieved_issued"] / 2500.0, rel=1e-3)
+    # MSE-only keys: no sign products
+    assert bench.decode_mfma_view(16, 8, 0, 1.0)["flops_per_launch_issued"] == 16 * 16384
 
 
 def test_encode_traffic_gate(bench, monkeypatch):

@@ -149,3 +149,37 @@ def test_chunk_workspace_sizing():
         T.chunk_workspace_bytes(1, 32, 8, 0, 100)
     with pytest.raises(T.TQError):
         T.chunk_workspace_bytes(1, 30, 8, 4, 100)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_split_codebook_tables_match_oracle(bits):
+    cb = T.Codebook(128, bits, 128, 0, 1, device=-1, wide_coords=64)
+    assert cb.split_info() == (64, bits + 1)
+    assert cb.code_words == (128 * bits + 64) // 32 and cb.sign_words == 4
+    book = O.build_split_book(128, bits, 64)
+    wide, narrow = cb.export_wide(), cb.export()
+    np.testing.assert_array_equal(wide["centroids"], book["wide"][0])
+    np.testing.assert_array_equal(wide["thresholds"], book["wide"][1])
+    np.testing.assert_array_equal(narrow["centroids"], book["narrow"][0])
+    np.testing.assert_array_equal(narrow["thresholds"], book["narrow"][1])
+    # the same seeds give the same Pi and S as a uniform codebook
+    u = T.Codebook(128, bits, 128, 0, 1, device=-1).export()
+    np.testing.assert_array_equal(narrow["rotation"], u["rotation"])
+    np.testing.assert_array_equal(narrow["qjl"], u["qjl"])
+
+
+def test_split_codebook_validation():
+    lib = _lib()
+    h = ctypes.c_void_p()
+    INV, UNS = T.api.TQ_ERR_INVALID_ARG, T.api.TQ_ERR_UNSUPPORTED
+    assert lib.tq_codebook_build_split(128, 4, 64, 0, 0, 1, -1, ctypes.byref(h)) == INV   # b' + 1 = 5
+    assert lib.tq_codebook_build_split(128, 2, 129, 0, 0, 1, -1, ctypes.byref(h)) == INV  # past d
+    assert lib.tq_codebook_build_split(128, 2, -1, 0, 0, 1, -1, ctypes.byref(h)) == INV
+    assert lib.tq_codebook_build_split(128, 2, 32, 0, 0, 1, 0, ctypes.byref(h)) == UNS   # GPU: 0 or 64 only
+    assert not h.value
+    # host-only: any count; a uniform handle has no wide tables
+    cb = T.Codebook(16, 2, 0, 0, 1, device=-1, wide_coords=5)
+    assert cb.split_info() == (5, 3) and cb.code_words == (16 * 2 + 5 + 31) // 32
+    assert T.Codebook(128, 2, 0, 0, 1, device=-1).split_info() == (0, 0)
+    with pytest.raises(T.TQError):
+        T.Codebook(128, 2, 0, 0, 1, device=-1).export_wide()
