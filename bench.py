@@ -40,7 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 
-# HBM bytes per key-encode launch on the 8B layer (262144 vectors), from two
+# HBM bytes per key-encode launch, from two
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this benchmark with
 # --calib-copy 512, each scaled by the ratio of a 512 MiB device copy's known
 # bytes to what the same counter read for it.  Valid only for the encode
@@ -50,9 +50,12 @@ HBM_PEAK_GBPS = 8000.0
 # busy fractions (SQ_VALU_MFMA_BUSY_CYCLES over 1,024 SIMDs x kernel cycles;
 # SQ_ACTIVE_INST_VALU less MFMA instructions at 4 cycles each).
 ENCODE_COUNTERS = {
-    "llama3-8b-layer-b1-s32768": {"source_sha256": "d6229989d1b4806eb7617f864ab0e949205112be30e940cbffb24cf6b395f4f0",
-                                  "fetch_bytes": 68507571, "write_bytes": 14710275,
-                                  "mfma_busy": 0.338, "valu_busy": 0.336},
+    "llama3-8b-layer-b1-s32768": {"source_sha256": "ee9783532cf990b4e6d086113c12f3663ca9087670e8f3aeb3e10c2c1569ce47",
+                                  "fetch_bytes": 68508992, "write_bytes": 14703014,
+                                  "mfma_busy": 0.339, "valu_busy": 0.337},
+    "bulk-encode-16777216-kv-then-decode-g8-s262144": {
+        "source_sha256": "ee9783532cf990b4e6d086113c12f3663ca9087670e8f3aeb3e10c2c1569ce47",
+        "fetch_bytes": 4296383888, "write_bytes": 1208072768, "mfma_busy": 0.486, "valu_busy": 0.476},
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 BULK_NAME = "bulk-encode-16777216-kv-then-decode-g8-s262144"
@@ -209,14 +212,7 @@ def bench_layer(args, T, dev, name, append_steps=0, chunk=0, logits=True, cpu=Tr
         kc, vc = caches[i_c]
         T.decode_attention(kcb, vcb, q, kc, vc, seq, out=out, workspace=ws, stream=stream)
 
-    if args.calib_copy:
-        n_el = args.calib_copy << 18           # MiB of float32
-        src = torch.ones(n_el, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calib_copy(args, dev)
 
     # fill every cache replica once (untimed), then warm up
     for i in range(n_cache):
@@ -330,6 +326,21 @@ def bench_layer(args, T, dev, name, append_steps=0, chunk=0, logits=True, cpu=Tr
     return line
 
 
+def calib_copy(args, dev):
+    """--calib-copy: three plain device copies of known size (untimed), the
+    reference launches that scale the HBM byte counters."""
+    import torch
+    if not args.calib_copy:
+        return
+    n_el = args.calib_copy << 18           # MiB of float32
+    src = torch.ones(n_el, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_bulk(args, T, dev, cpu=True):
     """Prefill-scale bulk encode: every step encodes 16,777,216 K vectors (b' = 3
     + QJL) and 16,777,216 V vectors (4-bit), then decodes 64 q heads (8 per kv
@@ -372,6 +383,7 @@ def bench_bulk(args, T, dev, cpu=True):
         if marks:
             marks[3].record(stream)
 
+    calib_copy(args, dev)
     for _ in range(max(1, args.warmup)):
         step()
     steps = max(1, args.steps)

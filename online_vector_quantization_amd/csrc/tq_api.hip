@@ -600,7 +600,7 @@ tq_status prepare_decode(const tq_codebook *kcb, const tq_codebook *vcb, const v
   if (a.k_split != a.v_split)
     return fail(TQ_ERR_UNSUPPORTED, "split widths need both codebooks split (keys %d, values %d wide coordinates)",
                 kcb->host.n_wide, vcb->host.n_wide);
-  if (a.v_split && !tq::mdecode_applies(a))
+  if (a.v_split && !tq::mdecode_can_run(a))
     return fail(TQ_ERR_UNSUPPORTED, "split-width values are read by the single-query matrix-core decode only: "
                 "t_cap a multiple of 4, 16-byte aligned norm arrays");
   *out_args = a;

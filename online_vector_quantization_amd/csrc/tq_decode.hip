@@ -1111,8 +1111,9 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
-  // single queries: the matrix-core decode; chunks of queries below the
-  // matrix-core chunk kernel's size: this file's per-query kernel
+  // single queries where the matrix cores are faster (mdecode_applies): the
+  // matrix-core decode; other single queries, and chunks of queries below the
+  // matrix-core chunk kernel's size: this file's per-head kernel
   const hipError_t e = mdecode_applies(a) ? launch_mdecode_main(a, false, stream) : launch_main<false>(a, stream);
   if (e != hipSuccess || (a.n_chunks == 1 && a.seq_inc == nullptr)) return e;   // one chunk per row: no merge
   hipLaunchKernelGGL(combine_out_kernel, dim3(a.batch * a.n_q_heads * a.n_new), dim3(kOutThreads), 0, stream, a);

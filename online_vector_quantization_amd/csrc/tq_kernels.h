@@ -174,11 +174,21 @@ hipError_t launch_mdecode_main(const DecodeArgs &a, bool scores_only, hipStream_
 // Rows up to this many tokens take the matrix-core decode (its per-lane cache
 // offsets are 32-bit byte offsets within a row: 72 bytes per token at most).
 constexpr int64_t kMDecodeMaxTcap = (int64_t{1} << 31) / 72;
-// Single-query decodes over rows of a multiple of 4 tokens (up to
-// kMDecodeMaxTcap) with 16-byte aligned norm arrays take the matrix-core
-// decode; others take the per-head vector decode.
-inline bool mdecode_applies(const DecodeArgs &a) {
+// Whether the matrix-core decode can read these arguments: single queries
+// over rows of a multiple of 4 tokens (up to kMDecodeMaxTcap) with 16-byte
+// aligned norm arrays.
+inline bool mdecode_can_run(const DecodeArgs &a) {
   return a.n_new == 1 && a.t_cap <= kMDecodeMaxTcap && a.norm_vec4 != 0;
+}
+// Which decode serves a call (decode, logits and the decode-loop step alike):
+// the matrix-core decode where it is measured faster -- g = 8, and g = 4 with
+// 3- or 4-bit key codes -- and for split widths, which only it reads; the
+// per-head vector decode otherwise (at g = 4 with 1- or 2-bit key codes its
+// nibble tables cost less than the matrix-core tile: 8B layer 27.8 against
+// 33.3 us, batched b = 2 57.7 against 67.8 us).
+inline bool mdecode_applies(const DecodeArgs &a) {
+  const int g = a.n_q_heads / a.n_kv_heads;
+  return mdecode_can_run(a) && (a.k_split || a.v_split || g == 8 || (g == 4 && a.k_bits >= 3));
 }
 // Scores only: the decode's key phase, writing every l_t to a.scores (no value
 // phase, no combine; the value fields are not read).

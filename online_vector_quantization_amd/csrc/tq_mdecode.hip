@@ -867,7 +867,7 @@ hipError_t launch_k(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
 
 hipError_t launch_mdecode_main(const DecodeArgs &a, bool scores_only, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
-  if (!mdecode_applies(a) || a.n_chunks > kMaxDecodeChunks || g < 1 || g > 8 || a.n_kv_heads > 65535 ||
+  if (!mdecode_can_run(a) || a.n_chunks > kMaxDecodeChunks || g < 1 || g > 8 || a.n_kv_heads > 65535 ||
       a.mk_lut == nullptr || a.rot_k_t == nullptr || (a.qjl_m > 0 && (a.qjl_rot_t == nullptr || a.sg_lut == nullptr)) ||
       (!scores_only && a.mv_lut == nullptr) || (a.k_split && a.mk_lut_w == nullptr) ||
       (!scores_only && (a.v_split != a.k_split || (a.v_split && a.mv_lut_w == nullptr))))
