@@ -214,7 +214,9 @@ template <int B> struct SplitRec {
 // token (tiles past seq_len are masked when used), byte offsets are 32-bit
 // on a uniform row base, and the norms come four at a time (the row length
 // is a multiple of 4 and the norm arrays 16-byte aligned on this path).
-template <int KB, int VB, bool QJL, bool SC, bool SPL>
+// PART selects what is loaded: the key side (bit 0: codes, signs, norms,
+// residual norms) and / or the value side (bit 1: value fields and norms).
+template <int PART, int KB, int VB, bool QJL, bool SC, bool SPL>
 __device__ __forceinline__ void load_tile(const DecodeArgs &a, int64_t row0, int tb, int n, int kq, bool lo_col,
                                           Tile<KB, VB, QJL, SC, SPL> &r) {
   // words per record
@@ -222,8 +224,11 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, int64_t row0, int
   constexpr int VW = SPL ? split_code_words(VB) : 4 * VB;
   const int last = static_cast<int>(a.t_cap) - 1;
   const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k_codes + row0 * KW);
+  // four consecutive tokens 4 kq .. 4 kq + 3 of the lane's own half (aligned
+  // to 4; a group past the row's end repeats its last group, masked later)
+  const uint32_t t4 = static_cast<uint32_t>(min(tb + 16 * (lo_col ? 1 : 0) + 4 * kq, last - 3)) * 4u;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+  for (int hf = 0; hf < 2 && (PART & 1); ++hf) {
     const uint32_t tk = static_cast<uint32_t>(min(tb + 16 * hf + n, last));
     if constexpr (SPL) {
       // the lane's 16 W wide bits lie within words w0, w0 + 1 (the second
@@ -247,16 +252,15 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, int64_t row0, int
       r.sg[hf] = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const unsigned char *>(a.k_signs + row0 * 4) +
                                                      (tk * 4u + kq) * 4u);
   }
-  // four consecutive tokens 4 kq .. 4 kq + 3 of the lane's own half (aligned
-  // to 4; a group past the row's end repeats its last group, masked later)
-  const uint32_t t4 = static_cast<uint32_t>(min(tb + 16 * (lo_col ? 1 : 0) + 4 * kq, last - 3)) * 4u;
-  const float4 nv = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(a.k_norms + row0) + t4);
-  r.knu[0] = nv.x; r.knu[1] = nv.y; r.knu[2] = nv.z; r.knu[3] = nv.w;
-  if constexpr (QJL) {
-    const float4 gv = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(a.k_res + row0) + t4);
-    r.gam[0] = gv.x; r.gam[1] = gv.y; r.gam[2] = gv.z; r.gam[3] = gv.w;
+  if constexpr ((PART & 1) != 0) {
+    const float4 nv = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(a.k_norms + row0) + t4);
+    r.knu[0] = nv.x; r.knu[1] = nv.y; r.knu[2] = nv.z; r.knu[3] = nv.w;
+    if constexpr (QJL) {
+      const float4 gv = *reinterpret_cast<const float4 *>(reinterpret_cast<const unsigned char *>(a.k_res + row0) + t4);
+      r.gam[0] = gv.x; r.gam[1] = gv.y; r.gam[2] = gv.z; r.gam[3] = gv.w;
+    }
   }
-  if constexpr (!SC) {
+  if constexpr (!SC && (PART & 2) != 0) {
     const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v_codes + row0 * VW);
     if constexpr (SPL) {
       // wide field: 4 W bits from word vw, narrow: 4 N bits from word vn; a
@@ -373,8 +377,8 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   // The wave's first tile is requested before the prologue, whose work then
   // hides its memory latency.
   Tile<KB, VB, QJL, SC, SPL> ta{};
-  int t0 = t_begin + wave * kTile;
-  if (t0 < t_end) load_tile<KB, VB, QJL, SC, SPL>(a, row0, t0, n, kq, lo_col, ta);
+  const int t0 = t_begin + wave * kTile;
+  if (t0 < t_end) load_tile<3, KB, VB, QJL, SC, SPL>(a, row0, t0, n, kq, lo_col, ta);
 
   // ------------------------------------------------------------ prologue
   // Striped copies of the codebooks' tables (key code pairs -> fp16 (hi, lo)
@@ -527,7 +531,9 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   const int sh_vn = (SPL && !SC) ? SplitRec<VB>::val_narrow_bit(n) & 31 : 0;
 
   // One tile: scores (key and sign products), online softmax, value product.
-  auto compute = [&](const Tile<KB, VB, QJL, SC, SPL> &cur, int tb) {
+  // Scores of one tile: l2[e] = the score (log2 units) of token 4 kq + e of
+  // the lane's own half, -inf past the row's end; written out when asked.
+  auto score_tile = [&](const Tile<KB, VB, QJL, SC, SPL> &cur, int tb, float (&l2)[4]) {
     const bool full = tb + kTile <= t_end;
     // ---- scores C[token 4 kq + e][column n] of both halves.  K-element
     // pair i of k-step s is (hi, lo) of coordinate 32 kq + 4 s + i (keys), or
@@ -585,7 +591,6 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
     // ---- the head's full score: its two columns summed across lanes n and
     // n ^ 8; lanes of columns 0..7 keep the first half's tokens, 8..15 the second's
     const int tk0 = tb + 16 * (lo_col ? 1 : 0) + 4 * kq;
-    float l2[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float y = (lo_col ? sacc[1][e] : sacc[0][e]) + swap8(lo_col ? sacc[0][e] : sacc[1][e]);
@@ -603,6 +608,12 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
           if (full || tk0 + e < t_end) sp[tk0 + e] = l2[e] * kLn2;
       }
     }
+  };
+
+  // Online softmax of one tile's scores and its value products.
+  auto value_tile = [&](const Tile<KB, VB, QJL, SC, SPL> &cur, const float (&l2)[4], int tb) {
+    const bool full = tb + kTile <= t_end;
+    const int tk0 = tb + 16 * (lo_col ? 1 : 0) + 4 * kq;
     if constexpr (!SC) {
       // ---- online softmax, running max raised lazily (wave-uniform decision)
       const float tmax = fmaxf(fmaxf(l2[0], l2[1]), fmaxf(l2[2], l2[3]));
@@ -716,13 +727,42 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
 
   constexpr int kStride = kWaves * kTile;
   Tile<KB, VB, QJL, SC, SPL> tn{};
-  // two tile buffers in turn: one is computed while the next is loaded
-  for (; t0 < t_end; t0 += 2 * kStride) {
-    if (t0 + kStride < t_end) load_tile<KB, VB, QJL, SC, SPL>(a, row0, t0 + kStride, n, kq, lo_col, tn);
-    compute(ta, t0);
-    if (t0 + kStride >= t_end) break;
-    if (t0 + 2 * kStride < t_end) load_tile<KB, VB, QJL, SC, SPL>(a, row0, t0 + 2 * kStride, n, kq, lo_col, ta);
-    compute(tn, t0 + kStride);
+  if constexpr (SC) {
+    // scores only: two key buffers in turn, one scored while the next loads
+    for (int tt = t0; tt < t_end; tt += 2 * kStride) {
+      float l2[4];
+      if (tt + kStride < t_end) load_tile<1, KB, VB, QJL, SC, SPL>(a, row0, tt + kStride, n, kq, lo_col, tn);
+      score_tile(ta, tt, l2);
+      if (tt + kStride >= t_end) break;
+      if (tt + 2 * kStride < t_end) load_tile<1, KB, VB, QJL, SC, SPL>(a, row0, tt + 2 * kStride, n, kq, lo_col, ta);
+      score_tile(tn, tt + kStride, l2);
+    }
+  } else if (t0 < t_end) {
+    // Software pipeline over the wave's tiles: the value phase of tile i and
+    // the score phase of tile i + 1 are independent and form one basic block
+    // (after the softmax's rescale branch), so the lookups and products of one
+    // run under the other's.  Buffer ta / tn alternate: while one holds tile
+    // i's values and the other tile i + 1's keys, tile i + 1's values and tile
+    // i + 2's keys load into the free halves.  Loads past the row's end read
+    // its last token (in bounds); their scores are masked to -inf, and the
+    // last step scores one such tile that nothing uses.
+    load_tile<1, KB, VB, QJL, SC, SPL>(a, row0, t0 + kStride, n, kq, lo_col, tn);
+    float la[4], lb[4];
+    score_tile(ta, t0, la);
+    for (int tt = t0;;) {
+      load_tile<2, KB, VB, QJL, SC, SPL>(a, row0, tt + kStride, n, kq, lo_col, tn);
+      load_tile<1, KB, VB, QJL, SC, SPL>(a, row0, tt + 2 * kStride, n, kq, lo_col, ta);
+      value_tile(ta, la, tt);
+      score_tile(tn, tt + kStride, lb);
+      tt += kStride;
+      if (tt >= t_end) break;
+      load_tile<2, KB, VB, QJL, SC, SPL>(a, row0, tt + kStride, n, kq, lo_col, ta);
+      load_tile<1, KB, VB, QJL, SC, SPL>(a, row0, tt + 2 * kStride, n, kq, lo_col, tn);
+      value_tile(tn, lb, tt);
+      score_tile(ta, tt + kStride, la);
+      tt += kStride;
+      if (tt >= t_end) break;
+    }
   }
 
   if constexpr (SC) return;   // uniform: no barrier follows for any thread
