@@ -186,9 +186,10 @@ tq_status upload_tables(tq_codebook *cb) {
   std::memcpy(img.data() + cb->off_centroids, h.centroids.data(), h.centroids.size() * sizeof(float));
   std::memcpy(img.data() + cb->off_thresholds, h.thresholds.data(), h.thresholds.size() * sizeof(float));
   // split widths: Pi's output rows and S's input columns follow the encode's
-  // split coordinate order (the wide coordinates in blocks 0..3)
-  tq::pack_encode_fragments(h.rotation.data(), img.data() + cb->off_rot_frag, split, false);
-  if (m > 0) tq::pack_encode_fragments(h.qjl.data(), img.data() + cb->off_qjl_frag, false, split);
+  // split coordinate order (the wide coordinates in blocks 0..3); the QJL
+  // fragments hold -S (the encode takes each sign bit from -p)
+  tq::pack_encode_fragments(h.rotation.data(), img.data() + cb->off_rot_frag, split, false, false);
+  if (m > 0) tq::pack_encode_fragments(h.qjl.data(), img.data() + cb->off_qjl_frag, false, split, true);
   std::memcpy(img.data() + cb->off_rot_f32, h.rotation.data(), h.rotation.size() * sizeof(float));
   float *rt = reinterpret_cast<float *>(img.data() + cb->off_rot_t_f32);
   for (int i = 0; i < d; ++i)

@@ -63,11 +63,11 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// (w << 1) | [p > 0] as one compare and one add with carry.
-__device__ __forceinline__ uint32_t shift_in_positive(uint32_t w, float p) {
-  uint32_t r;
-  asm volatile("v_cmp_lt_f32 vcc, 0, %1\n\tv_addc_co_u32 %0, vcc, %2, %2, vcc" : "=v"(r) : "v"(p), "v"(w) : "vcc");
-  return r;
+// (w << 1) | (the sign bit of np): with np = -p (the QJL fragments hold -S),
+// that bit is [p > 0] for every p but NaN (and -0, which an accumulator started
+// at +0 cannot produce), in one funnel shift.
+__device__ __forceinline__ uint32_t shift_in_sign(uint32_t w, float np) {
+  return __builtin_amdgcn_alignbit(w, __float_as_uint(np), 31);
 }
 
 // Round 8 floats to bf16 (RNE) and return hi and lo = bf16(v - hi).
@@ -230,7 +230,7 @@ hipError_t launch_bits(const EncodeArgs &a, bool qjl, bool x_f32, int num_cus, h
 
 }  // namespace
 
-void pack_encode_fragments(const float *mat, void *dst, bool split_rows, bool split_cols) {
+void pack_encode_fragments(const float *mat, void *dst, bool split_rows, bool split_cols, bool negate) {
   // Element (t, s, lane, e) of a split is A[row][col] of the 16x16x32 MFMA tile
   // t, k-step s: lane % 16 picks output row enc_coord(i / 4, t, i % 4) with
   // i = lane % 16 (the coordinate that lane group i / 4 receives), element e
@@ -245,7 +245,7 @@ void pack_encode_fragments(const float *mat, void *dst, bool split_rows, bool sp
             const int i = lane & 15, kq = lane >> 4;
             const int row = enc_coord(split_rows, i >> 2, t, i & 3);
             const int col = enc_coord(split_cols, kq, 2 * s + (e >> 2), e & 3);
-            const float v = mat[row * kHeadDim + col];
+            const float v = negate ? -mat[row * kHeadDim + col] : mat[row * kHeadDim + col];
             const uint16_t hi = bf16_bits_rne(v);
             const uint16_t val = split == 0 ? hi : bf16_bits_rne(v - bf16_bits_to_float(hi));
             out[((((split * 8 + t) * 4 + s) * 64 + lane) * 8) + e] = val;

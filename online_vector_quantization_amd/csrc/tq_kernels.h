@@ -55,7 +55,7 @@ struct EncodeArgs {
   float *dbg_rot;
   float *dbg_proj;
   const uint4 *frag_rot;   // kFragBytes
-  const uint4 *frag_qjl;   // kFragBytes (keys with QJL)
+  const uint4 *frag_qjl;   // kFragBytes (keys with QJL): fragments of -S
   const float4 *qlut;      // kQuantCellEntries quantizer cells
   const float4 *qlut_wide; // split widths: the wide codebook's cells (else null)
   float qscale, qbias;     // cell = min(uint(y * qscale + qbias), kQuantCellEntries - 1)
@@ -65,8 +65,9 @@ struct EncodeArgs {
 // row-major matrix `mat` (rows = outputs, columns = inputs).  split_rows puts
 // the output rows in the split coordinate order of enc_coord (the rotation's
 // outputs are the rotated coordinates); split_cols does so for the input
-// columns (S's inputs are the rotated residual's coordinates).
-void pack_encode_fragments(const float *mat, void *dst, bool split_rows, bool split_cols);
+// columns (S's inputs are the rotated residual's coordinates).  negate packs
+// -mat (the QJL matrix: the encode then reads -p, whose sign bit is the sketch).
+void pack_encode_fragments(const float *mat, void *dst, bool split_rows, bool split_cols, bool negate);
 
 // Builds the quantizer cell table (4 floats per cell); false if the
 // thresholds do not fit the cell grid (then the GPU path is unsupported).
