@@ -149,3 +149,27 @@ def test_split_llama8b_layer_full():
     T.encode_into_cache(vcb, H.to_device(wl.v.reshape(-1, 128), "bf16"), vc)
     err = H.check_decode(kcb, vcb, H.to_device(wl.q, "bf16"), kc, vc, [wl.seq_len], 2, 3, 128, wide=WIDE)
     _log(f"  decode max-abs error {err:.2e}")
+
+
+def test_split_edge_cases():
+    """Split widths at the smallest row (t_cap = 4), empty and full sequences,
+    g = 8, fp32 queries, bf16 output (the RNE rounding of the fp32 output), and
+    the allocation-free entry point (bit-equal to the workspace one)."""
+    rng = np.random.default_rng(460)
+    for (B, Hkv, g, t_cap, lens, qdt) in ((2, 1, 8, 4, [4, 0], "f32"), (3, 2, 2, 8, [0, 8, 3], "bf16")):
+        k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap))
+        v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap))
+        qf = rng.standard_normal((B, Hkv * g, 128)).astype(np.float32)
+        q = H.to_device(qf if qdt == "f32" else synth.bf16_bits(qf), qdt)
+        _log(f"split edge B={B} Hkv={Hkv} g={g} t_cap={t_cap} lens={lens} q={qdt}")
+        kcb, vcb = H.gpu_book(1, 128, WIDE), H.gpu_book(2, 0, WIDE)
+        kc, vc = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, t_cap, t_cap)
+        H.check_decode(kcb, vcb, q, kc, vc, lens, 1, 2, 128, wide=WIDE)
+        sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+        a = T.decode_attention(kcb, vcb, q, kc, vc, sl)
+        s = T.decode_attention_static(kcb, vcb, q, kc, vc, sl)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(a.cpu().numpy().view(np.uint32), s.cpu().numpy().view(np.uint32))
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.all(a[b].cpu().numpy() == 0.0)
