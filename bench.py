@@ -50,12 +50,12 @@ HBM_PEAK_GBPS = 8000.0
 # busy fractions (SQ_VALU_MFMA_BUSY_CYCLES over 1,024 SIMDs x kernel cycles;
 # SQ_ACTIVE_INST_VALU less MFMA instructions at 4 cycles each).
 ENCODE_COUNTERS = {
-    "llama3-8b-layer-b1-s32768": {"source_sha256": "ee9783532cf990b4e6d086113c12f3663ca9087670e8f3aeb3e10c2c1569ce47",
-                                  "fetch_bytes": 68508992, "write_bytes": 14703014,
-                                  "mfma_busy": 0.339, "valu_busy": 0.337},
+    "llama3-8b-layer-b1-s32768": {"source_sha256": "344bfa705087a3b458f905a3032535374a3a914f393d56501082a3246cd41703",
+                                  "fetch_bytes": 68504660, "write_bytes": 14692925,
+                                  "mfma_busy": 0.343, "valu_busy": 0.325},
     "bulk-encode-16777216-kv-then-decode-g8-s262144": {
-        "source_sha256": "ee9783532cf990b4e6d086113c12f3663ca9087670e8f3aeb3e10c2c1569ce47",
-        "fetch_bytes": 4296383888, "write_bytes": 1208072768, "mfma_busy": 0.486, "valu_busy": 0.476},
+        "source_sha256": "344bfa705087a3b458f905a3032535374a3a914f393d56501082a3246cd41703",
+        "fetch_bytes": 4296375995, "write_bytes": 1207993173, "mfma_busy": 0.493, "valu_busy": 0.46},
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 BULK_NAME = "bulk-encode-16777216-kv-then-decode-g8-s262144"
