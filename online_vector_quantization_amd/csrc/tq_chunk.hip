@@ -23,19 +23,17 @@
 // Tile kernel: work-group = (64 query rows of one kv head, chunk of tokens),
 // 8 waves (two per SIMD).  Row m of kv head hk is query j = m / g of q head
 // hk g + m % g, at position seq_len - n_new + j; it sees tokens below
-// clamp(seq_len - n_new + j + 1, 0, t_cap).  Per 128-token tile:
-//   1. the tile's key and value records are staged in LDS (and the next
-//      tile's are requested);
-//   2. the values are dequantized into a transposed (coordinate x token)
-//      bf16 hi/lo tile;
-//   3. wave (row half, token quarter) computes its 32 x 32 score block from
-//      key codes dequantized straight into MFMA operands, scales and masks
-//      it, and stores it in LDS;
-//   4. eight threads per row run the online softmax over the 128 tokens and
-//      store P = p nu^v as bf16 hi/lo;
-//   5. wave (row half, coordinate quarter) rescales (when a running max
-//      moved) and accumulates its 32 x 32 output block: P x V.
-// The chunk's (max, sum, rotated output) per row go to the workspace in the
+// clamp(seq_len - n_new + j + 1, 0, t_cap).  The tokens are split among the
+// waves (split-K): wave (row half, quarter) takes 32 of every 128 tokens for
+// its 32 rows and keeps its own softmax state and output, so a step needs no
+// barrier and no score or weight tile in LDS.  Per 32-token step it
+//   1. forms the transposed scores (tokens x rows) from key codes dequantized
+//      straight into MFMA operands, scales them, masks causally;
+//   2. runs the online softmax of each row (one lane pair per row) and turns
+//      the weights P = p nu^v into bf16 hi/lo operands in registers;
+//   3. accumulates O^T += V^T P^T, dequantizing its own value records.
+// At the end the four quarters of each row half merge through LDS, and the
+// chunk's (max, sum, rotated output) per row go to the workspace in the
 // decode's partial layout.
 #include <hip/hip_runtime.h>
 
@@ -48,18 +46,20 @@ namespace tq {
 namespace {
 
 constexpr int D = kHeadDim;
-constexpr int kRows = 64;               // query rows per work-group
-constexpr int kTile = 128;              // tokens per tile
-constexpr int kThreads = 512;           // 8 waves
-constexpr int kSmT = kThreads / kRows;  // softmax threads per row (16 tokens each)
-constexpr int kVtStride = kTile + 8;    // bf16 per coordinate row of the value tile (16 B pad)
-constexpr int kPStride = kTile + 8;     // bf16 per row of P
-constexpr int kScStride = kTile + 4;    // floats per row of the score tile
+constexpr int kRows = 64;               // query rows per work-group: two halves of 32
+constexpr int kStep = 32;               // tokens per wave step
+constexpr int kQuart = 4;               // waves per row half, each a quarter of every kTile tokens
+constexpr int kTile = kStep * kQuart;   // 128: token chunks are whole multiples of this
+constexpr int kWaves = 2 * kQuart;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kQpStride = 2 * D;        // floats per query row in the prep buffer: q~ then s
 constexpr int kSStride = D + 8;         // bf16 per row of the LDS copy of s (16 B pad)
-// A row's running max is raised only when a score exceeds it by more than
-// this (weights stay <= e^8), so most tiles rescale nothing.
-constexpr float kLazy = 8.f;
+constexpr int kSlot = 64 * 65;          // floats per wave in the final merge: 64 registers x 64 lanes, rows of 65
+// A row's running max (log2 units) is raised only when a score exceeds it by
+// more than this (weights stay <= 2^12), so most steps rescale nothing.
+constexpr float kLazy2 = 12.f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -142,36 +142,55 @@ __global__ __launch_bounds__(kQpThreads) void qprep_kernel(DecodeArgs a) {
   }
 }
 
-template <int KB, bool QJL>
+// Split-K tile kernel.  Wave (row half mh, quarter kq) owns rows
+// m0 + 32 mh .. + 31 and tokens t_begin + 32 kq + 128 i .. + 31 of its chunk;
+// it keeps its own running max, sum and output for its rows, and the four
+// quarters of a row half merge once, at the end.
+//
+// Per 32-token step the wave forms the transposed scores S^T (tokens x rows)
+// with v_mfma_f32_32x32x16_bf16: A = the key codes dequantized per token
+// (lane = token, coordinates 64 hi + 8 ks .. + 7 at k-step ks, one
+// pair-table lookup per two codes), B = q~ of the rows (lane = row, the same
+// coordinates, in registers), three passes hi*hi + hi*lo + lo*hi; the QJL
+// term takes A = the signs (+-1, exact), B = s from LDS, two passes.  In this
+// layout a lane holds 16 tokens of one row, so the row's softmax needs one
+// exchange with the lane 32 away, and its weights P are already the B operand
+// of the value product O^T += V^T P^T (coordinates x rows), whose A operand,
+// lane = coordinate group, dequantizes the tokens that P's k index runs over.
+// Nothing passes through LDS per step but the wave's own value records and
+// per-token factors, read back by its own lanes (LDS accesses of one wave
+// complete in order, so no barrier is needed).
+template <int KB, int VB, bool QJL>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
-  constexpr int KW = D * KB / 32;       // key code words per token
-  constexpr int kKMask = (1 << (2 * KB)) - 1;
-  __shared__ uint2 s_kpair[1 << (2 * KB)];     // two key codes -> (hi pair, lo pair)
-  __shared__ uint2 s_vpair[256];               // two value codes -> (hi pair, lo pair)
-  __shared__ uint32_t s_kc[kTile * KW];
-  __shared__ uint32_t s_sg[QJL ? kTile * 4 : 1];
-  __shared__ float s_knu[kTile], s_gam[kTile], s_vnu[kTile];
-  __shared__ uint32_t s_vc[kTile * 16];
-  __shared__ __align__(16) uint16_t s_vth[D * kVtStride];
-  __shared__ __align__(16) uint16_t s_vtl[D * kVtStride];
-  // the score tile and P share one region: the softmax reads every score
-  // into registers, waits, then writes P
-  __shared__ __align__(16) union {
-    float sc[kRows * kScStride];
-    struct {
-      uint16_t h[kRows * kPStride];
-      uint16_t l[kRows * kPStride];
-    } p;
-  } s_tile;
-  float *const s_sc = s_tile.sc;
-  uint16_t *const s_ph = s_tile.p.h;
-  uint16_t *const s_pl = s_tile.p.l;
-  __shared__ float s_alpha[kRows];
-  // the QJL query operand s as bf16 hi/lo, [row][coordinate]: read per k-step
-  // (in registers it would not fit beside q~ at two waves per SIMD)
-  __shared__ __align__(16) uint16_t s_sh[QJL ? kRows * kSStride : 8];
-  __shared__ __align__(16) uint16_t s_sl[QJL ? kRows * kSStride : 8];
-  __shared__ int s_rescale;   // some row of the tile raised its running max
+  constexpr int KH = 2 * KB;              // key code words per half record (64 coordinates)
+  constexpr int KW = 2 * KH;
+  constexpr int VW = 4 * VB;              // value code words per token
+  constexpr int kKP = 1 << (2 * KB), kVP = 1 << (2 * VB);
+  constexpr uint32_t kKMask = kKP - 1, kVMask = (1u << VB) - 1;
+  constexpr int kVst = kStep * VW + 4;    // a wave's value records (+ the word past the last one)
+  // The hi and lo halves of a pair-table entry sit in two arrays whose
+  // distance the pad keeps out of reach of a merged two-address LDS read, so
+  // each half loads straight into its MFMA operand register.
+  struct Smem {
+    uint32_t kh[kKP + 1];
+    uint32_t pad0[300];
+    uint32_t kl[kKP + 1];
+    uint32_t vh[kVP + 1];
+    uint32_t pad1[300];
+    uint32_t vl[kVP + 1];
+    alignas(16) uint4 sgn[QJL ? 256 : 1];   // sign byte -> eight bf16 +-1 (set bit: +1)
+    alignas(16) float ml[kWaves][32][2];    // per wave and row: running max (log2 units), sum
+    alignas(16) union {
+      struct {
+        uint16_t sh[QJL ? kRows * kSStride : 8];   // s as bf16 hi, [row][coordinate]
+        uint16_t sl[QJL ? kRows * kSStride : 8];   // and lo
+        uint32_t vst[kWaves][kVst];                // each wave's value records of its step
+        float fac[kWaves][3][kStep];               // per token: scale log2(e) nu, coef gamma, nu^v
+      } loop;
+      float slot[kWaves][kSlot];   // each wave's output scaled to the row half's max: [register][lane], rows of 65
+    } u;
+  };
+  __shared__ Smem sm;
 
   const int g = a.n_q_heads / a.n_kv_heads;
   const int rows_total = g * a.n_new;
@@ -182,10 +201,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
   const int b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int mblk = wave & 1;             // row half (scores and P x V)
-  const int nb = wave >> 1;              // token quarter (scores)
-  const int cb = wave >> 1;              // 32-coordinate block (P x V)
-  const int VB = a.v_bits, VW = 4 * VB;
+  const int mh = wave & 1, kq = wave >> 1;
   const int row_id = b * a.n_kv_heads + hk;
   const int64_t row0 = static_cast<int64_t>(row_id) * a.t_cap;
   const int t_cap = static_cast<int>(a.t_cap);
@@ -199,23 +215,27 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
   const int t_begin = chunk_id * a.chunk;
   const int t_end = min(win(min(m0 + kRows, rows_total) - 1), t_begin + a.chunk);
 
-  // ---- prologue: pair tables, query operands, state
-  {
-    for (int e = tid; e <= kKMask; e += kThreads) {
-      uint32_t h2, l2;
-      split_pair(a.k_pair[2 * e], a.k_pair[2 * e + 1], h2, l2);
-      s_kpair[e] = make_uint2(h2, l2);
-    }
-    for (int e = tid; e < (1 << (2 * VB)); e += kThreads) {
-      uint32_t h2, l2;
-      split_pair(a.v_lut[2 * e], a.v_lut[2 * e + 1], h2, l2);
-      s_vpair[e] = make_uint2(h2, l2);
-    }
+  // ---- prologue: pair and sign tables, s in LDS, q~ in registers
+  for (int e = tid; e < kKP; e += kThreads) {
+    uint32_t h2, l2;
+    split_pair(a.k_pair[2 * e], a.k_pair[2 * e + 1], h2, l2);
+    sm.kh[e] = h2;
+    sm.kl[e] = l2;
   }
-  // A operands of the scores: row 32 mblk + l32 of the block, coordinates
-  // 16 ks + 8 hi .. + 7 of q~ (and of s)
-  bf16x8 qa_h[8], qa_l[8];
+  for (int e = tid; e < kVP; e += kThreads) {
+    uint32_t h2, l2;
+    split_pair(a.v_lut[2 * e], a.v_lut[2 * e + 1], h2, l2);
+    sm.vh[e] = h2;
+    sm.vl[e] = l2;
+  }
   if constexpr (QJL) {
+    for (int e = tid; e < 256; e += kThreads) {
+      uint32_t z[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        z[p] = 0xBF80BF80u ^ (((e >> (2 * p)) & 1u) << 15) ^ (((e >> (2 * p + 1)) & 1u) << 31);
+      sm.sgn[e] = make_uint4(z[0], z[1], z[2], z[3]);
+    }
     // thread: row tid / 8, coordinates 16 (tid % 8) .. + 15 of s
     const int r = tid >> 3, c0 = 16 * (tid & 7);
     const bool live = m0 + r < rows_total;
@@ -227,264 +247,338 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
       split_pair(v.x, v.y, h[2 * k4], l[2 * k4]);
       split_pair(v.z, v.w, h[2 * k4 + 1], l[2 * k4 + 1]);
     }
-    uint4 *dh = reinterpret_cast<uint4 *>(&s_sh[r * kSStride + c0]);
-    uint4 *dl = reinterpret_cast<uint4 *>(&s_sl[r * kSStride + c0]);
+    uint4 *dh = reinterpret_cast<uint4 *>(&sm.u.loop.sh[r * kSStride + c0]);
+    uint4 *dl = reinterpret_cast<uint4 *>(&sm.u.loop.sl[r * kSStride + c0]);
     dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
     dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
     dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
     dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
   }
+  // B operands of the scores: row m0 + 32 mh + l32, coordinates 64 hi + 8 ks .. + 7 of q~
+  const int mrow = m0 + 32 * mh + l32;
+  const bool row_live = mrow < rows_total;
+  bf16x8 qb_h[8], qb_l[8];
   {
-    const int mq = m0 + 32 * mblk + l32;
-    const bool live = mq < rows_total;
-    const float *qp = a.ws_qprep + (static_cast<int64_t>(row_id) * rows_total + (live ? mq : 0)) * kQpStride;
+    const float *qp = a.ws_qprep + (static_cast<int64_t>(row_id) * rows_total + (row_live ? mrow : 0)) * kQpStride + 64 * hi;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-      if (live) {
-        x0 = *reinterpret_cast<const float4 *>(qp + 16 * ks + 8 * hi);
-        x1 = *reinterpret_cast<const float4 *>(qp + 16 * ks + 8 * hi + 4);
+      if (row_live) {
+        x0 = *reinterpret_cast<const float4 *>(qp + 8 * ks);
+        x1 = *reinterpret_cast<const float4 *>(qp + 8 * ks + 4);
       }
       uint32_t h[4], l[4];
       split_pair(x0.x, x0.y, h[0], l[0]);
       split_pair(x0.z, x0.w, h[1], l[1]);
       split_pair(x1.x, x1.y, h[2], l[2]);
       split_pair(x1.z, x1.w, h[3], l[3]);
-      qa_h[ks] = as_bf16x8(h[0], h[1], h[2], h[3]);
-      qa_l[ks] = as_bf16x8(l[0], l[1], l[2], l[3]);
+      qb_h[ks] = as_bf16x8(h[0], h[1], h[2], h[3]);
+      qb_l[ks] = as_bf16x8(l[0], l[1], l[2], l[3]);
     }
   }
-  // softmax role: row sm of the block, tokens 16 sq .. 16 sq + 15 of a tile
-  const int sm = tid / kSmT, sq = tid % kSmT;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 o;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) o[r] = 0.f;
+  __syncthreads();
 
-  // A tile's records, one thread's share (tokens past the tile's end read as
-  // zero codes): at most one uint4 of key codes and one of value codes (a
-  // tile holds 32 KW and 32 VW of them), and for threads < 128 the token's
-  // sign words and norms.  Loaded one tile ahead.
+  const bool wave_live = m0 + 32 * mh < rows_total;
+  const int w_first = wave_live ? win(m0 + 32 * mh) : 0;   // the smallest window of the wave's rows
+  const int w_row = row_live ? win(mrow) : 0;
+  // value operand: A-row l32 of block cb is coordinate 4 l32 + cb, whose
+  // four codes are 4 VB bits at this offset of a token's record
+  const int vwo = (4 * VB * l32) >> 5, vsh = (4 * VB * l32) & 31;
+  uint32_t *const vst = sm.u.loop.vst[wave];
+  float (&fac)[3][kStep] = sm.u.loop.fac[wave];
+
+  float m_run = -INFINITY, l_lane = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[cb][r] = 0.f;
+
+  // One step's records in registers, loaded one step ahead.  Lane (token
+  // l32, half hi): that token's key codes and signs of coordinates 64 hi ..
+  // + 63 and its factors (tokens past t_end read the last valid one, masked
+  // below); the value records of the step's 32 tokens, one contiguous block,
+  // lane L its words 2 VB L .. + 2 VB - 1 (words of missing tokens read as 0).
   struct Rec {
-    uint4 kc, vc, sg;
-    float knu, vnu, gam;
+    uint32_t kc[KH];
+    uint32_t sg[2];
+    float nu, gq, nv;
+    uint32_t vw[2 * VB];
   };
-  auto load_tile = [&](int t0) {
+  const float nu_scale = a.scale * kLog2e;
+  auto load_step = [&](int t0) {
     Rec r;
-    const int nt = min(kTile, t_end - t0);
-    r.kc = make_uint4(0u, 0u, 0u, 0u);
-    r.vc = r.kc;
-    r.sg = r.kc;
-    r.knu = r.vnu = r.gam = 0.f;
-    if (tid < kTile * KW / 4 && tid / (KW / 4) < nt)
-      r.kc = reinterpret_cast<const uint4 *>(a.k_codes + (row0 + t0) * KW)[tid];
-    if (tid < kTile * VW / 4 && tid / VB < nt) r.vc = reinterpret_cast<const uint4 *>(a.v_codes + (row0 + t0) * VW)[tid];
-    if (tid < nt) {
-      r.knu = a.k_norms[row0 + t0 + tid];
-      r.vnu = a.v_norms[row0 + t0 + tid];
-      if constexpr (QJL) {
-        r.gam = a.k_res[row0 + t0 + tid];
-        r.sg = reinterpret_cast<const uint4 *>(a.k_signs)[row0 + t0 + tid];
+    const int tok = min(t0 + l32, t_end - 1);
+    const int64_t row = row0 + tok;
+    const uint32_t *kp = a.k_codes + row * KW + KH * hi;
+    if constexpr (KH % 4 == 0) {
+#pragma unroll
+      for (int w = 0; w < KH / 4; ++w) {
+        const uint4 x = reinterpret_cast<const uint4 *>(kp)[w];
+        r.kc[4 * w] = x.x;
+        r.kc[4 * w + 1] = x.y;
+        r.kc[4 * w + 2] = x.z;
+        r.kc[4 * w + 3] = x.w;
       }
+    } else {
+#pragma unroll
+      for (int w = 0; w < KH / 2; ++w) {
+        const uint2 x = reinterpret_cast<const uint2 *>(kp)[w];
+        r.kc[2 * w] = x.x;
+        r.kc[2 * w + 1] = x.y;
+      }
+    }
+    r.sg[0] = r.sg[1] = 0u;
+    r.gq = 0.f;
+    if constexpr (QJL) {
+      const uint2 x = reinterpret_cast<const uint2 *>(a.k_signs + row * (kQjlDim / 32))[hi];
+      r.sg[0] = x.x;
+      r.sg[1] = x.y;
+      r.gq = a.qjl_coef * a.k_res[row];
+    }
+    r.nu = nu_scale * a.k_norms[row];
+    r.nv = a.v_norms[row];
+    const int nvalid = min(kStep, t_end - t0) * VW;
+    const uint32_t *vp = a.v_codes + (row0 + t0) * VW;
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+      const int w = 2 * VB * lane + 2 * u;
+      const uint2 x = w < nvalid ? *reinterpret_cast<const uint2 *>(vp + w) : make_uint2(0u, 0u);
+      r.vw[2 * u] = x.x;
+      r.vw[2 * u + 1] = x.y;
     }
     return r;
   };
-  Rec nxt{};
-  if (t_begin < t_end) nxt = load_tile(t_begin);
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    // ---- 1. stage the records; the previous tile's readers of these
-    // buffers finished before its softmax barrier
-    if (tid < kTile * KW / 4) reinterpret_cast<uint4 *>(s_kc)[tid] = nxt.kc;
-    if (tid < kTile * VW / 4) reinterpret_cast<uint4 *>(s_vc)[tid] = nxt.vc;
-    if (tid < kTile) {
-      s_knu[tid] = nxt.knu;
-      s_vnu[tid] = nxt.vnu;
+  int t0 = t_begin + kStep * kq;
+  Rec cur{};
+  if (wave_live && t0 < t_end) cur = load_step(t0);
+  for (; wave_live && t0 < t_end; t0 += kTile) {
+    // stage the step's value records and factors (this wave's reads of the
+    // previous step's were issued before these writes)
+#pragma unroll
+    for (int u = 0; u < VB; ++u)
+      *reinterpret_cast<uint2 *>(vst + 2 * VB * lane + 2 * u) = make_uint2(cur.vw[2 * u], cur.vw[2 * u + 1]);
+    if (hi == 0) {
+      fac[0][l32] = cur.nu;
+      fac[1][l32] = cur.gq;
+      fac[2][l32] = cur.nv;
+    }
+    Rec nxt = cur;
+    if (t0 + kTile < t_end) nxt = load_step(t0 + kTile);
+
+    // ---- scores S^T: C row = token 8 (r / 4) + 4 hi + r % 4 of the step, column = row l32
+    f32x16 sacc, tacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sacc[r] = 0.f;
+      tacc[r] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      // codes of coordinates 64 hi + 8 ks .. + 7: 8 KB bits of the half record
+      constexpr int kBits = 8 * KB;
+      const int bit = kBits * ks, w = bit >> 5, shf = bit & 31;
+      uint32_t bits;
+      if (shf + kBits > 32)
+        bits = __builtin_amdgcn_alignbit(cur.kc[w + 1], cur.kc[w], shf);
+      else
+        bits = cur.kc[w] >> shf;
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t idx = (bits >> (2 * KB * p)) & kKMask;
+        h[p] = sm.kh[idx];
+        l[p] = sm.kl[idx];
+      }
+      const bf16x8 ka_h = as_bf16x8(h[0], h[1], h[2], h[3]);
+      const bf16x8 ka_l = as_bf16x8(l[0], l[1], l[2], l[3]);
+      sacc = mfma(ka_h, qb_h[ks], sacc);
+      sacc = mfma(ka_h, qb_l[ks], sacc);
+      sacc = mfma(ka_l, qb_h[ks], sacc);
       if constexpr (QJL) {
-        s_gam[tid] = nxt.gam;
-        reinterpret_cast<uint4 *>(s_sg)[tid] = nxt.sg;
+        const uint32_t byte = (cur.sg[ks >> 2] >> (8 * (ks & 3))) & 0xffu;
+        const bf16x8 z = __builtin_bit_cast(bf16x8, sm.sgn[byte]);
+        const int srow = (32 * mh + l32) * kSStride + 64 * hi + 8 * ks;
+        tacc = mfma(z, *reinterpret_cast<const bf16x8 *>(&sm.u.loop.sh[srow]), tacc);
+        tacc = mfma(z, *reinterpret_cast<const bf16x8 *>(&sm.u.loop.sl[srow]), tacc);
       }
     }
-    __syncthreads();
-    if (tid == 0) s_rescale = 0;   // every reader of the previous tile's flag is past this barrier
-    if (t0 + kTile < t_end) nxt = load_tile(t0 + kTile);
-
-    // ---- 2. values -> transposed bf16 hi/lo tile [coordinate][token]
-    {
-      const int tok = tid & (kTile - 1);
+    // logits in log2 units
+    float lg[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int grp = tid / kTile + 4 * i;   // coordinates 8 grp .. 8 grp + 7
-        const int bit = 8 * grp * VB;
-        const int w = bit >> 5, sh = bit & 31;
-        const uint32_t w0 = s_vc[tok * VW + w];
-        const uint32_t w1 = (sh + 8 * VB > 32) ? s_vc[tok * VW + w + 1] : 0u;
-        const uint32_t bits = __builtin_amdgcn_alignbit(w1, w0, sh);
-        const uint32_t pmask = (1u << (2 * VB)) - 1u;
+    for (int R = 0; R < 4; ++R) {
+      const float4 nu4 = *reinterpret_cast<const float4 *>(&fac[0][8 * R + 4 * hi]);
+      const float nuv[4] = {nu4.x, nu4.y, nu4.z, nu4.w};
+      float gqv[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (QJL) {
+        const float4 g4 = *reinterpret_cast<const float4 *>(&fac[1][8 * R + 4 * hi]);
+        gqv[0] = g4.x;
+        gqv[1] = g4.y;
+        gqv[2] = g4.z;
+        gqv[3] = g4.w;
+      }
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint2 e = s_vpair[(bits >> (2 * VB * p)) & pmask];
-          const int c = 8 * grp + 2 * p;
-          s_vth[c * kVtStride + tok] = static_cast<uint16_t>(e.x);
-          s_vth[(c + 1) * kVtStride + tok] = static_cast<uint16_t>(e.x >> 16);
-          s_vtl[c * kVtStride + tok] = static_cast<uint16_t>(e.y);
-          s_vtl[(c + 1) * kVtStride + tok] = static_cast<uint16_t>(e.y >> 16);
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * R + u;
+        const float dot = QJL ? fmaf(gqv[u], tacc[r], sacc[r]) : sacc[r];
+        lg[r] = nuv[u] * dot;
       }
     }
-
-    // ---- 3. scores of rows 32 mblk .., tokens 32 nb + l32
-    {
-      const int tk = 32 * nb + l32;
-      f32x16 sacc, tacc;
+    if (t0 + kStep > w_first) {   // some token of the step is past some row's window
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[r] = 0.f;
-        tacc[r] = 0.f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        // codes of coordinates 16 ks + 8 hi .. + 7: 8 KB bits
-        const int bit = (16 * ks + 8 * hi) * KB;
-        const int w = bit >> 5, sh = bit & 31;
-        const uint32_t w0 = s_kc[tk * KW + w];
-        const uint32_t w1 = (sh + 8 * KB > 32) ? s_kc[tk * KW + w + 1] : 0u;
-        const uint32_t bits = __builtin_amdgcn_alignbit(w1, w0, sh);
-        uint32_t bh[4], bl[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint2 e = s_kpair[(bits >> (2 * KB * p)) & kKMask];
-          bh[p] = e.x;
-          bl[p] = e.y;
-        }
-        const bf16x8 kb_h = as_bf16x8(bh[0], bh[1], bh[2], bh[3]);
-        const bf16x8 kb_l = as_bf16x8(bl[0], bl[1], bl[2], bl[3]);
-        sacc = mfma(qa_h[ks], kb_h, sacc);
-        sacc = mfma(qa_h[ks], kb_l, sacc);
-        sacc = mfma(qa_l[ks], kb_h, sacc);
-        if constexpr (QJL) {
-          // signs 16 ks + 8 hi .. + 7 as bf16 +-1 (set bit: +1)
-          const uint32_t b8 = (s_sg[tk * 4 + (ks >> 1)] >> (16 * (ks & 1) + 8 * hi)) & 0xffu;
-          uint32_t z[4];
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            z[p] = 0xBF80BF80u ^ (((b8 >> (2 * p)) & 1u) << 15) ^ (((b8 >> (2 * p + 1)) & 1u) << 31);
-          const bf16x8 zb = as_bf16x8(z[0], z[1], z[2], z[3]);
-          const int srow = (32 * mblk + l32) * kSStride + 16 * ks + 8 * hi;
-          tacc = mfma(*reinterpret_cast<const bf16x8 *>(&s_sh[srow]), zb, tacc);
-          tacc = mfma(*reinterpret_cast<const bf16x8 *>(&s_sl[srow]), zb, tacc);
-        }
-      }
-      const float nu = s_knu[tk];
-      const float gq = QJL ? a.qjl_coef * s_gam[tk] : 0.f;
-      const int t = t0 + tk;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int mr = 32 * mblk + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int m = m0 + mr;
-        const bool live = m < rows_total && t < t_end && t < win(m);
-        const float dot = QJL ? fmaf(gq, tacc[r], sacc[r]) : sacc[r];
-        s_sc[mr * kScStride + tk] = live ? a.scale * nu * dot : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (t0 + 8 * (r >> 2) + 4 * hi + (r & 3) >= w_row) lg[r] = -INFINITY;
     }
-    __syncthreads();
 
-    // ---- 4. online softmax, kSmT (8) threads per row
-    {
-      float lv[16];
+    // ---- online softmax of row mrow: lanes l32 and l32 + 32 hold its 32 tokens
+    float mx = lg[0];
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const float4 v = *reinterpret_cast<const float4 *>(&s_sc[sm * kScStride + 16 * sq + 4 * k4]);
-        lv[4 * k4] = v.x;
-        lv[4 * k4 + 1] = v.y;
-        lv[4 * k4 + 2] = v.z;
-        lv[4 * k4 + 3] = v.w;
-      }
-      float mx = lv[0];
-#pragma unroll
-      for (int k = 1; k < 16; ++k) mx = fmaxf(mx, lv[k]);
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
-      mx = fmaxf(mx, __shfl_xor(mx, 2));
-      mx = fmaxf(mx, __shfl_xor(mx, 4));
-      // lazy max: raised only past m_run + kLazy (alpha = 1 otherwise)
-      const bool grow = mx > m_run + kLazy;
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, lg[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run + kLazy2)) {
+      const bool grow = mx > m_run + kLazy2;
       const float m_new = grow ? mx : m_run;
-      const float alpha = grow ? __expf(m_run - m_new) : 1.f;   // exp(-inf) = 0 for a first max
-      if (grow) s_rescale = 1;
-      float ls = 0.f;
-      uint32_t ph[8], pl[8];
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_lane *= alpha;
 #pragma unroll
-      for (int k = 0; k < 16; k += 2) {
-        const float p0 = (lv[k] == -INFINITY) ? 0.f : __expf(lv[k] - m_new);
-        const float p1 = (lv[k + 1] == -INFINITY) ? 0.f : __expf(lv[k + 1] - m_new);
-        ls += p0 + p1;
-        split_pair(p0 * s_vnu[16 * sq + k], p1 * s_vnu[16 * sq + k + 1], ph[k / 2], pl[k / 2]);
-      }
-      ls += __shfl_xor(ls, 1);
-      ls += __shfl_xor(ls, 2);
-      ls += __shfl_xor(ls, 4);
-      l_run = l_run * alpha + ls;
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
       m_run = m_new;
-      __syncthreads();   // every score is read: P may overwrite them
-      uint4 *dh = reinterpret_cast<uint4 *>(&s_ph[sm * kPStride + 16 * sq]);
-      uint4 *dl = reinterpret_cast<uint4 *>(&s_pl[sm * kPStride + 16 * sq]);
-      dh[0] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-      dh[1] = make_uint4(ph[4], ph[5], ph[6], ph[7]);
-      dl[0] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-      dl[1] = make_uint4(pl[4], pl[5], pl[6], pl[7]);
-      if (sq == 0) s_alpha[sm] = alpha;
     }
-    __syncthreads();
-    const bool rescale = s_rescale != 0;
+    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+    // P = p nu^v as bf16 hi/lo B operands: k-step s takes registers 8 s .. 8 s + 7
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      const float4 v4 = *reinterpret_cast<const float4 *>(&fac[2][8 * R + 4 * hi]);
+      const float nvv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int u = 0; u < 4; u += 2) {
+        const int r = 4 * R + u;
+        const float p0 = __builtin_amdgcn_exp2f(lg[r] - mref);
+        const float p1 = __builtin_amdgcn_exp2f(lg[r + 1] - mref);
+        l_lane += p0 + p1;
+        split_pair(p0 * nvv[u], p1 * nvv[u + 1], ph[r >> 1], pl[r >> 1]);
+      }
+    }
 
-    // ---- 5. o = alpha o + P x V for rows 32 mblk .., coordinates 32 cb ..
-    {
-      if (rescale) {
+    // ---- O^T += V^T P^T: A-row l32 of block cb = coordinate 4 l32 + cb; k
+    // index 8 hi + e of k-step s = token 16 s + 8 (e / 4) + 4 hi + e % 4
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[r] *= s_alpha[32 * mblk + 8 * (r >> 2) + 4 * hi + (r & 3)];
+    for (int s = 0; s < 2; ++s) {
+      uint32_t gw[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = 16 * s + 8 * (e >> 2) + 4 * hi + (e & 3);
+        const uint32_t *rp = vst + tok * VW + vwo;
+        if constexpr (VB == 3)
+          gw[e] = __builtin_amdgcn_alignbit(rp[1], rp[0], vsh);
+        else
+          gw[e] = rp[0] >> vsh;
       }
+      const bf16x8 pb_h = as_bf16x8(ph[4 * s], ph[4 * s + 1], ph[4 * s + 2], ph[4 * s + 3]);
+      const bf16x8 pb_l = as_bf16x8(pl[4 * s], pl[4 * s + 1], pl[4 * s + 2], pl[4 * s + 3]);
 #pragma unroll
-      for (int ks = 0; ks < kTile / 16; ++ks) {
-        const int prow = (32 * mblk + l32) * kPStride + 16 * ks + 8 * hi;
-        const bf16x8 pa_h = *reinterpret_cast<const bf16x8 *>(&s_ph[prow]);
-        const bf16x8 pa_l = *reinterpret_cast<const bf16x8 *>(&s_pl[prow]);
-        const int vrow = (32 * cb + l32) * kVtStride + 16 * ks + 8 * hi;
-        const bf16x8 vb_h = *reinterpret_cast<const bf16x8 *>(&s_vth[vrow]);
-        const bf16x8 vb_l = *reinterpret_cast<const bf16x8 *>(&s_vtl[vrow]);
-        o = mfma(pa_h, vb_h, o);
-        o = mfma(pa_h, vb_l, o);
-        o = mfma(pa_l, vb_h, o);
+      for (int cb = 0; cb < 4; ++cb) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t idx = ((gw[2 * u] >> (VB * cb)) & kVMask) | (((gw[2 * u + 1] >> (VB * cb)) & kVMask) << VB);
+          h[u] = sm.vh[idx];
+          l[u] = sm.vl[idx];
+        }
+        const bf16x8 va_h = as_bf16x8(h[0], h[1], h[2], h[3]);
+        const bf16x8 va_l = as_bf16x8(l[0], l[1], l[2], l[3]);
+        o[cb] = mfma(va_h, pb_h, o[cb]);
+        o[cb] = mfma(va_h, pb_l, o[cb]);
+        o[cb] = mfma(va_l, pb_h, o[cb]);
       }
     }
+    cur = nxt;
   }
 
-  // ---- the chunk's partials, in the decode's layout: group (query row of
-  // (b, kv head, j), chunk), then head h
-  const int nc = a.n_chunks;
+  // ---- merge of the four quarters of each row half, then the chunk's partials
+  // in the decode's layout: group (query row of (b, kv head, j), chunk), then head h
+  {
+    const float l_row = l_lane + __shfl_xor(l_lane, 32);
+    if (hi == 0) {
+      sm.ml[wave][l32][0] = m_run;
+      sm.ml[wave][l32][1] = l_row;
+    }
+  }
+  __syncthreads();   // every wave is past its loop: the slots may overwrite the loop's LDS
+  {
+    float M = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = m0 + 32 * mblk + 8 * (r >> 2) + 4 * hi + (r & 3);
+    for (int q = 0; q < kQuart; ++q) M = fmaxf(M, sm.ml[2 * q + mh][l32][0]);
+    const float sc = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+    float *slot = sm.u.slot[wave];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) slot[(r + 16 * cb) * 65 + lane] = o[cb][r] * sc;
+  }
+  __syncthreads();
+  {
+    // thread: row R of the block, coordinates 16 (tid % 8) .. + 15
+    const int R = tid >> 3, c0 = 16 * (tid & 7);
+    const int rmh = R >> 5, rj = R & 31;
+    const int m = m0 + R;
     if (m < rows_total) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kQuart; ++q) M = fmaxf(M, sm.ml[2 * q + rmh][rj][0]);
+      float out[16];
+#pragma unroll
+      for (int c16 = 0; c16 < 16; ++c16) {
+        // coordinate c: block cb = c % 4, A-row i = c / 4 = 8 (r / 4) + 4 hh + r % 4
+        const int c = c0 + c16, i = c >> 2, cb = c & 3;
+        const int r = 4 * (i >> 3) + (i & 3), ln = rj + 32 * ((i >> 2) & 1);
+        float v = 0.f;
+#pragma unroll
+        for (int q = 0; q < kQuart; ++q) v += sm.u.slot[2 * q + rmh][(r + 16 * cb) * 65 + ln];
+        out[c16] = v;
+      }
+      const int nc = a.n_chunks;
       const int64_t grp = (static_cast<int64_t>(row_id) * a.n_new + m / g) * nc + chunk_id;
-      a.ws_part_o[(grp * g + m % g) * D + 32 * cb + l32] = o[r];
+      float4 *dst = reinterpret_cast<float4 *>(a.ws_part_o + (grp * g + m % g) * D + c0);
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) dst[k4] = make_float4(out[4 * k4], out[4 * k4 + 1], out[4 * k4 + 2], out[4 * k4 + 3]);
+      if ((tid & 7) == 0) {
+        float L = 0.f;
+#pragma unroll
+        for (int q = 0; q < kQuart; ++q) {
+          const float mq = sm.ml[2 * q + rmh][rj][0];
+          if (mq != -INFINITY) L += sm.ml[2 * q + rmh][rj][1] * __builtin_amdgcn_exp2f(mq - M);
+        }
+        a.ws_part_ml[(grp * g + m % g) * 2] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+        a.ws_part_ml[(grp * g + m % g) * 2 + 1] = L;
+      }
     }
   }
-  if (sq == 0 && m0 + sm < rows_total) {
-    const int m = m0 + sm;
-    const int64_t grp = (static_cast<int64_t>(row_id) * a.n_new + m / g) * nc + chunk_id;
-    a.ws_part_ml[(grp * g + m % g) * 2] = m_run;
-    a.ws_part_ml[(grp * g + m % g) * 2 + 1] = l_run;
+}
+
+template <int KB, int VB>
+hipError_t launch_tiles_v(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+  if (a.qjl_m > 0) {
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, true>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((chunk_kernel<KB, VB, false>), grid, dim3(kThreads), 0, stream, a);
   }
+  return hipGetLastError();
 }
 
 template <int KB>
 hipError_t launch_tiles(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
-  if (a.qjl_m > 0) {
-    hipLaunchKernelGGL((chunk_kernel<KB, true>), grid, dim3(kThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((chunk_kernel<KB, false>), grid, dim3(kThreads), 0, stream, a);
+  switch (a.v_bits) {
+    case 1: return launch_tiles_v<KB, 1>(a, grid, stream);
+    case 2: return launch_tiles_v<KB, 2>(a, grid, stream);
+    case 3: return launch_tiles_v<KB, 3>(a, grid, stream);
+    case 4: return launch_tiles_v<KB, 4>(a, grid, stream);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
