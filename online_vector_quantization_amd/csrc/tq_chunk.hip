@@ -85,6 +85,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t w0, uint32_t w1, uint32_t w
   return __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
 }
 
+// v combined with the value of lane l ^ 32 (one v_permlane32_swap): every lane
+// gets op(v[l mod 32], v[l mod 32 + 32]) bit for bit
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float load_query(const void *q, int q_bf16, int64_t idx) {
   if (q_bf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(q)[idx]) << 16);
   return static_cast<const float *>(q)[idx];
@@ -435,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
     float mx = lg[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, lg[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     if (__any(mx > m_run + kLazy2)) {
       const bool grow = mx > m_run + kLazy2;
       const float m_new = grow ? mx : m_run;
@@ -502,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
   // ---- merge of the four quarters of each row half, then the chunk's partials
   // in the decode's layout: group (query row of (b, kv head, j), chunk), then head h
   {
-    const float l_row = l_lane + __shfl_xor(l_lane, 32);
+    const float l_row = sum_halves(l_lane);
     if (hi == 0) {
       sm.ml[wave][l32][0] = m_run;
       sm.ml[wave][l32][1] = l_row;

@@ -862,88 +862,101 @@ __global__ __launch_bounds__(Geom<G>::kThreads) void decode_kernel(DecodeArgs a)
   }
 }
 
-// Merge of the chunks of one (b, q head) for the matrix-core chunk kernel,
-// whose partial outputs stay rotated: log-sum-exp weights, rotated sum, then
-// o = Pi_v^T o~.  A separate launch: the kernel boundary makes every chunk's
-// partials visible across XCDs without an in-kernel device fence.  Every
-// global read (the chunks' (max, sum), their partial outputs and this
-// thread's slice of Pi_v) is issued before the first barrier.
+// Merge of the chunks for the matrix-core chunk kernel, whose partial outputs
+// stay rotated: log-sum-exp weights, rotated sums, then o = Pi_v^T o~.  A
+// work-group merges the g rows of one (b, kv head, query), so it reads Pi_v
+// once for all of them; a launch of its own, whose boundary makes every
+// chunk's partials visible across XCDs without an in-kernel device fence.
+// Every global read (this thread's slice of Pi_v and its rows' partial
+// outputs) is issued before the chunk weights are formed.
 constexpr int kCombThreads = 512;
-constexpr int kCombPer = kMaxDecodeChunks / 4;   // partial outputs per thread
+constexpr int kCombRegs = 32;   // partial outputs per row held in registers; more chunks are read in a loop
 
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
-  __shared__ float s_w[kMaxDecodeChunks];
-  __shared__ float s_l[kMaxDecodeChunks];
-  __shared__ float s_o[4][D];
-  __shared__ float s_r[4][D];
-  __shared__ float s_scal[2];
-  const int bhq = blockIdx.x;                  // (b * Hq + q head) * n_new + query
-  const int jq = bhq % a.n_new;
-  const int b = bhq / a.n_new / a.n_q_heads;
-  const int hq = bhq / a.n_new % a.n_q_heads;
+  __shared__ float s_w[8][kMaxDecodeChunks];   // row h: chunk weights divided by the total
+  __shared__ float s_o[8][D];                  // row h: merged rotated sum
+  __shared__ float s_r[4][8][D];               // quarter products of Pi_v^T
+  const int qrow = blockIdx.x;                 // (b * Hkv + kv head) * n_new + query
+  const int jq = qrow % a.n_new;
+  const int bhk = qrow / a.n_new;
+  const int b = bhk / a.n_kv_heads, hk = bhk % a.n_kv_heads;
   const int g = a.n_q_heads / a.n_kv_heads;
-  const int hk = hq / g, h = hq % g;
-  const int qrow = (b * a.n_kv_heads + hk) * a.n_new + jq;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nc = a.n_chunks;
   const int64_t grp0 = static_cast<int64_t>(qrow) * nc;
-  // thread (i, quarter): output coordinate i; chunks quarter, quarter + 4, ...;
-  // Pi_v rows 32 quarter .. 32 quarter + 31 of column i
+  const int64_t cstride = static_cast<int64_t>(g) * D;
+  // thread (i, quarter): rows quarter and quarter + 4 at coordinate i, then
+  // Pi_v rows 32 quarter .. 32 quarter + 31 of column i for every row
   const int i = tid & (D - 1), quarter = tid >> 7;
+  const int h0 = quarter, h1 = quarter + 4;
+  const bool has0 = h0 < g, has1 = h1 < g;
   float pv[32];
 #pragma unroll
   for (int jj = 0; jj < 32; ++jj) pv[jj] = a.rot_v[(32 * quarter + jj) * D + i];
-  float po[kCombPer];
+  const float *pb0 = a.ws_part_o + (grp0 * g + h0) * D + i;
+  const float *pb1 = a.ws_part_o + (grp0 * g + h1) * D + i;
+  float po0[kCombRegs], po1[kCombRegs];
 #pragma unroll
-  for (int k = 0; k < kCombPer; ++k) {
-    const int c = quarter + 4 * k;
-    po[k] = (c < nc) ? a.ws_part_o[((grp0 + c) * g + h) * D + i] : 0.f;
+  for (int c = 0; c < kCombRegs; ++c) {
+    po0[c] = (has0 && c < nc) ? pb0[c * cstride] : 0.f;
+    po1[c] = (has1 && c < nc) ? pb1[c * cstride] : 0.f;
   }
-  if (tid < nc) {
-    const float m = a.ws_part_ml[((grp0 + tid) * g + h) * 2];
-    const float l = a.ws_part_ml[((grp0 + tid) * g + h) * 2 + 1];
-    s_w[tid] = (l > 0.f) ? m : -INFINITY;
-    s_l[tid] = l;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float mx = -INFINITY;
-    for (int c = tid; c < nc; c += 64) mx = fmaxf(mx, s_w[c]);
-    mx = wave_max(mx);
-    float tot = 0.f;
-    for (int c = tid; c < nc; c += 64) {
-      const float w = (s_w[c] == -INFINITY) ? 0.f : __expf(s_w[c] - mx);
-      s_w[c] = w;
-      tot += w * s_l[c];
+  // wave h < g: the chunk weights of row h (lane c: chunks c and c + 64)
+  if (wave < g) {
+    const int h = wave;
+    float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
+    if (lane < nc) {
+      m0 = a.ws_part_ml[((grp0 + lane) * g + h) * 2];
+      l0 = a.ws_part_ml[((grp0 + lane) * g + h) * 2 + 1];
     }
-    tot = wave_sum(tot);
-    if (tid == 0) s_scal[0] = (tot > 0.f) ? 1.f / tot : 0.f;
+    if (lane + 64 < nc) {
+      m1 = a.ws_part_ml[((grp0 + lane + 64) * g + h) * 2];
+      l1 = a.ws_part_ml[((grp0 + lane + 64) * g + h) * 2 + 1];
+    }
+    static_assert(kMaxDecodeChunks <= 128, "two chunk weights per lane");
+    if (!(l0 > 0.f)) m0 = -INFINITY;
+    if (!(l1 > 0.f)) m1 = -INFINITY;
+    const float mx = wave_max(fmaxf(m0, m1));
+    const float w0 = (m0 == -INFINITY) ? 0.f : __expf(m0 - mx);
+    const float w1 = (m1 == -INFINITY) ? 0.f : __expf(m1 - mx);
+    const float tot = wave_sum(w0 * l0 + w1 * l1);
+    const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
+    s_w[h][lane] = w0 * inv;
+    s_w[h][lane + 64] = w1 * inv;
   }
   __syncthreads();
-  const float inv = s_scal[0];
-  {
+  if (has0) {
     float o = 0.f;
 #pragma unroll
-    for (int k = 0; k < kCombPer; ++k) {
-      const int c = quarter + 4 * k;
-      if (c < nc) o = fmaf(s_w[c], po[k], o);
-    }
-    s_o[quarter][i] = o;
+    for (int c = 0; c < kCombRegs; ++c) o = fmaf(s_w[h0][c], po0[c], o);
+    for (int c = kCombRegs; c < nc; ++c) o = fmaf(s_w[h0][c], pb0[c * cstride], o);
+    s_o[h0][i] = o;
+  }
+  if (has1) {
+    float o = 0.f;
+#pragma unroll
+    for (int c = 0; c < kCombRegs; ++c) o = fmaf(s_w[h1][c], po1[c], o);
+    for (int c = kCombRegs; c < nc; ++c) o = fmaf(s_w[h1][c], pb1[c * cstride], o);
+    s_o[h1][i] = o;
   }
   __syncthreads();
-  {
+  for (int h = 0; h < g; ++h) {
     float r = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) {
-      const int j = 32 * quarter + jj;
-      r = fmaf(pv[jj], (s_o[0][j] + s_o[1][j] + s_o[2][j] + s_o[3][j]) * inv, r);
+    for (int j4 = 0; j4 < 8; ++j4) {
+      const float4 v = *reinterpret_cast<const float4 *>(&s_o[h][32 * quarter + 4 * j4]);
+      r = fmaf(pv[4 * j4], v.x, r);
+      r = fmaf(pv[4 * j4 + 1], v.y, r);
+      r = fmaf(pv[4 * j4 + 2], v.z, r);
+      r = fmaf(pv[4 * j4 + 3], v.w, r);
     }
-    s_r[quarter][i] = r;
+    s_r[quarter][h][i] = r;
   }
   __syncthreads();
-  if (tid < D) {
-    const float r = s_r[0][tid] + s_r[1][tid] + s_r[2][tid] + s_r[3][tid];
-    const int64_t o_idx = static_cast<int64_t>(bhq) * D + tid;
+  for (int e = tid; e < g * D; e += kCombThreads) {
+    const int h = e / D, c = e % D;
+    const float r = s_r[0][h][c] + s_r[1][h][c] + s_r[2][h][c] + s_r[3][h][c];
+    const int64_t o_idx = ((static_cast<int64_t>(b) * a.n_q_heads + hk * g + h) * a.n_new + jq) * D + c;
     if (a.out_bf16) {
       static_cast<uint16_t *>(a.out)[o_idx] = f32_to_bf16_rne(r);
     } else {
@@ -952,7 +965,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeArgs a) {
   }
   // Append steps: the sequence has one more cached token (the main kernel,
   // the only reader of seq_len, has completed).
-  if (a.seq_inc != nullptr && hq == 0 && jq == 0 && tid == 0) {
+  if (a.seq_inc != nullptr && hk == 0 && jq == 0 && tid == 0) {
     const int32_t s = a.seq_inc[b];
     if (s >= 0 && s < a.t_cap) a.seq_inc[b] = s + 1;
   }
@@ -1105,7 +1118,8 @@ DecodePlan plan_chunk(int batch, int n_q_heads, int n_kv_heads, int n_new, int64
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream) {
   if (a.n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_q_heads * a.n_new), dim3(kCombThreads), 0, stream, a);
+  if (a.n_q_heads / a.n_kv_heads > 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.n_kv_heads * a.n_new), dim3(kCombThreads), 0, stream, a);
   return hipGetLastError();
 }
 
