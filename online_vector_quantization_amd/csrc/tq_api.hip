@@ -544,6 +544,8 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
   a.scores = scores;
   a.rot_k_t = dev_ptr<float>(kcb, kcb->off_rot_t_f32);
   a.qjl_rot_t = m > 0 ? dev_ptr<float>(kcb, kcb->off_qjl_rot_t_f32) : nullptr;
+  a.k_frag_rot = dev_ptr<uint4>(kcb, kcb->off_rot_frag);
+  a.k_frag_qjl = m > 0 ? dev_ptr<uint4>(kcb, kcb->off_qjl_frag) : nullptr;
   a.k_lut = dev_ptr<float>(kcb, kcb->off_key_lut);
   a.k_pair = dev_ptr<float>(kcb, kcb->off_pair_lut);
   a.mk_lut = dev_ptr<void>(kcb, kcb->off_mkey_lut);
@@ -558,7 +560,6 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
   a.ws_qslot = reinterpret_cast<float *>(ws + plan.off_qslot);
   a.ws_part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
   a.ws_part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
-  a.ws_qprep = tq::chunk_uses_mfma(g, n_new) ? reinterpret_cast<float *>(ws + plan.off_qprep) : nullptr;
   a.chunk = plan.chunk;
   a.n_chunks = plan.n_chunks;
   *out_args = a;

@@ -16,12 +16,12 @@
 // operand is split as hi + lo (bf16 each) and a product takes the three
 // passes hi*hi + hi*lo + lo*hi; the +-1 signs are exact in bf16 (two passes).
 //
-// Launches: a query-prep kernel (q~ and s of every query row, fp32), the
-// tile kernel, and the decode's combine kernel (log-sum-exp merge of the
+// Launches: the tile kernel and a merge kernel (log-sum-exp merge of the
 // token chunks, Pi_v^T, output).
 //
 // Tile kernel: work-group = (64 query rows of one kv head, chunk of tokens),
-// 8 waves (two per SIMD).  Row m of kv head hk is query j = m / g of q head
+// 8 waves (two per SIMD).  Its prologue forms q~ and s of its rows on the
+// matrix cores from the codebook's bf16 hi/lo fragments of Pi_k and S.  Row m of kv head hk is query j = m / g of q head
 // hk g + m % g, at position seq_len - n_new + j; it sees tokens below
 // clamp(seq_len - n_new + j + 1, 0, t_cap).  The tokens are split among the
 // waves (split-K): wave (row half, quarter) takes 32 of every 128 tokens for
@@ -52,7 +52,6 @@ constexpr int kQuart = 4;               // waves per row half, each a quarter of
 constexpr int kTile = kStep * kQuart;   // 128: token chunks are whole multiples of this
 constexpr int kWaves = 2 * kQuart;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQpStride = 2 * D;        // floats per query row in the prep buffer: q~ then s
 constexpr int kSStride = D + 8;         // bf16 per row of the LDS copy of s (16 B pad)
 constexpr int kSlot = 64 * 65;          // floats per wave in the final merge: 64 registers x 64 lanes, rows of 65
 // A row's running max (log2 units) is raised only when a score exceeds it by
@@ -65,9 +64,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // (a, b) rounded to bf16 (nearest even): a in the low half.
@@ -94,63 +97,6 @@ __device__ __forceinline__ float max_halves(float v) {
 __device__ __forceinline__ float sum_halves(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float load_query(const void *q, int q_bf16, int64_t idx) {
-  if (q_bf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(q)[idx]) << 16);
-  return static_cast<const float *>(q)[idx];
-}
-
-// q~ = Pi_k q and s = (S Pi_k) q of the g query rows of one (b, kv head, j)
-// per work-group, written to rows ((b Hkv + hk) n_new + j) g + h of the prep
-// buffer.  Thread (column c, part pp): c < d is column c of Pi_k^T, d + i
-// column i of (S Pi_k)^T; part pp holds entries 32 pp .. 32 pp + 31 of it
-// (all reads issued before the first product) and forms their partial dot
-// products with all g queries, which the four parts then sum in LDS.  Each
-// matrix is read once per g rows, and each thread's chain is 32 long.
-constexpr int kQpParts = 4;
-constexpr int kQpThreads = 2 * D * kQpParts;
-constexpr int kQpSpan = D / kQpParts;   // matrix entries per thread
-
-template <bool QJL, int G>
-__global__ __launch_bounds__(kQpThreads) void qprep_kernel(DecodeArgs a) {
-  __shared__ float sq[G][D];
-  __shared__ float part[kQpParts][G][2 * D];
-  const int qrow = blockIdx.x;   // (b Hkv + hk) n_new + j
-  const int j = qrow % a.n_new;
-  const int bhk = qrow / a.n_new;
-  const int b = bhk / a.n_kv_heads, hk = bhk % a.n_kv_heads;
-  const int tid = threadIdx.x;
-  const int col = tid & (2 * D - 1), pp = tid / (2 * D);
-  const int i = col & (D - 1);
-  const bool active = col < D || QJL;   // uniform per wave (D is a multiple of 64)
-  const float *mat = col < D ? a.rot_k_t : a.qjl_rot_t;
-  float cv[kQpSpan];
-  if (active) {
-#pragma unroll
-    for (int jj = 0; jj < kQpSpan; ++jj) cv[jj] = mat[(kQpSpan * pp + jj) * D + i];
-  }
-  for (int e = tid; e < G * D; e += kQpThreads)
-    sq[e / D][e % D] =
-        load_query(a.q, a.q_bf16, (static_cast<int64_t>(b * a.n_q_heads + hk * G + e / D) * a.n_new + j) * D + e % D);
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float acc = 0.f;
-    if (active) {
-#pragma unroll
-      for (int jj = 0; jj < kQpSpan; ++jj) acc = fmaf(cv[jj], sq[h][kQpSpan * pp + jj], acc);
-    }
-    part[pp][h][col] = acc;
-  }
-  __syncthreads();
-  for (int e = tid; e < G * 2 * D; e += kQpThreads) {
-    const int h = e / (2 * D), c = e % (2 * D);
-    float v = 0.f;
-#pragma unroll
-    for (int q = 0; q < kQpParts; ++q) v += part[q][h][c];
-    a.ws_qprep[(static_cast<int64_t>(qrow) * G + h) * kQpStride + c] = v;
-  }
 }
 
 // Split-K tile kernel.  Wave (row half mh, quarter kq) owns rows
@@ -195,6 +141,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
       struct {
         uint16_t sh[QJL ? kRows * kSStride : 8];   // s as bf16 hi, [row][coordinate]
         uint16_t sl[QJL ? kRows * kSStride : 8];   // and lo
+        uint16_t qh[kRows * kSStride];             // prologue: q~ as bf16 hi, [row][coordinate]
+        uint16_t ql[kRows * kSStride];             // and lo
+        uint16_t xh[kRows * kSStride];             // prologue: the queries as bf16 hi, [row][coordinate]
+        uint16_t xl[kRows * kSStride];             // and lo
         uint32_t vst[kWaves][kVst];                // each wave's value records of its step
         float fac[kWaves][3][kStep];               // per token: scale log2(e) nu, coef gamma, nu^v
       } loop;
@@ -247,45 +197,109 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
         z[p] = 0xBF80BF80u ^ (((e >> (2 * p)) & 1u) << 15) ^ (((e >> (2 * p + 1)) & 1u) << 31);
       sm.sgn[e] = make_uint4(z[0], z[1], z[2], z[3]);
     }
-    // thread: row tid / 8, coordinates 16 (tid % 8) .. + 15 of s
+  }
+  // The block's queries into LDS as bf16 hi/lo (thread: row tid / 8,
+  // coordinates 16 (tid % 8) .. + 15; rows past the last read as zero).
+  const bool q_bf16 = a.q_bf16 != 0;
+  {
     const int r = tid >> 3, c0 = 16 * (tid & 7);
-    const bool live = m0 + r < rows_total;
-    const float *sp = a.ws_qprep + (static_cast<int64_t>(row_id) * rows_total + (live ? m0 + r : 0)) * kQpStride + D + c0;
+    const int m = m0 + r;
     uint32_t h[8], l[8];
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const float4 v = live ? reinterpret_cast<const float4 *>(sp)[k4] : make_float4(0.f, 0.f, 0.f, 0.f);
-      split_pair(v.x, v.y, h[2 * k4], l[2 * k4]);
-      split_pair(v.z, v.w, h[2 * k4 + 1], l[2 * k4 + 1]);
+    for (int k = 0; k < 8; ++k) h[k] = l[k] = 0u;
+    if (m < rows_total) {
+      const int64_t qi = (static_cast<int64_t>(b * a.n_q_heads + hk * g + m % g) * a.n_new + m / g) * D + c0;
+      // 4-byte reads: the query need only be 4-byte aligned
+      if (q_bf16) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(a.q) + qi);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) h[k] = src[k];
+      } else {
+        const float *src = static_cast<const float *>(a.q) + qi;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) split_pair(src[2 * k], src[2 * k + 1], h[k], l[k]);
+      }
     }
-    uint4 *dh = reinterpret_cast<uint4 *>(&sm.u.loop.sh[r * kSStride + c0]);
-    uint4 *dl = reinterpret_cast<uint4 *>(&sm.u.loop.sl[r * kSStride + c0]);
+    uint4 *dh = reinterpret_cast<uint4 *>(&sm.u.loop.xh[r * kSStride + c0]);
+    uint4 *dl = reinterpret_cast<uint4 *>(&sm.u.loop.xl[r * kSStride + c0]);
     dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
     dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
     dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
     dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
   }
+  // q~ = Pi_k q and s = S q~ of the block's rows on the matrix cores
+  // (v_mfma_f32_16x16x32_bf16), from the codebook's bf16 hi/lo operand
+  // fragments of Pi_k and of -S: wave t takes output tile t, whose lane
+  // (n, kq) receives coordinates 32 kq + 4 t .. + 3 of row n of an N-block,
+  // and reads each fragment once.  B operand: lane (n, kq), element e of
+  // k-step ks = input coordinate 32 kq + 8 ks + e of row n.  The products
+  // take the passes hi*hi + lo*hi (+ hi*lo for fp32 queries and for q~).
+  const int n16 = lane & 15, kq4 = lane >> 4;
+  const uint4 *fr = a.k_frag_rot;
+  bf16x8 fa_h[4], fa_l[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    fa_h[ks] = __builtin_bit_cast(bf16x8, fr[((0 * 8 + wave) * 4 + ks) * 64 + lane]);
+    fa_l[ks] = __builtin_bit_cast(bf16x8, fr[((1 * 8 + wave) * 4 + ks) * 64 + lane]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nb = 0; nb < kRows / 16; ++nb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int xo = (16 * nb + n16) * kSStride + 32 * kq4 + 8 * ks;
+      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&sm.u.loop.xh[xo]);
+      acc = mfma16(fa_h[ks], bh, acc);
+      acc = mfma16(fa_l[ks], bh, acc);
+      if (!q_bf16) acc = mfma16(fa_h[ks], *reinterpret_cast<const bf16x8 *>(&sm.u.loop.xl[xo]), acc);
+    }
+    uint32_t h0, l0, h1, l1;
+    split_pair(acc[0], acc[1], h0, l0);
+    split_pair(acc[2], acc[3], h1, l1);
+    const int qo = (16 * nb + n16) * kSStride + 32 * kq4 + 4 * wave;
+    *reinterpret_cast<uint2 *>(&sm.u.loop.qh[qo]) = make_uint2(h0, h1);
+    *reinterpret_cast<uint2 *>(&sm.u.loop.ql[qo]) = make_uint2(l0, l1);
+  }
+  if constexpr (QJL) {
+    const uint4 *fq = a.k_frag_qjl;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      fa_h[ks] = __builtin_bit_cast(bf16x8, fq[((0 * 8 + wave) * 4 + ks) * 64 + lane]);
+      fa_l[ks] = __builtin_bit_cast(bf16x8, fq[((1 * 8 + wave) * 4 + ks) * 64 + lane]);
+    }
+  }
+  __syncthreads();
+  if constexpr (QJL) {
+#pragma unroll
+    for (int nb = 0; nb < kRows / 16; ++nb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int xo = (16 * nb + n16) * kSStride + 32 * kq4 + 8 * ks;
+        const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&sm.u.loop.qh[xo]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&sm.u.loop.ql[xo]);
+        acc = mfma16(fa_h[ks], bh, acc);
+        acc = mfma16(fa_l[ks], bh, acc);
+        acc = mfma16(fa_h[ks], bl, acc);
+      }
+      uint32_t h0, l0, h1, l1;   // the fragments hold -S
+      split_pair(-acc[0], -acc[1], h0, l0);
+      split_pair(-acc[2], -acc[3], h1, l1);
+      const int so = (16 * nb + n16) * kSStride + 32 * kq4 + 4 * wave;
+      *reinterpret_cast<uint2 *>(&sm.u.loop.sh[so]) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2 *>(&sm.u.loop.sl[so]) = make_uint2(l0, l1);
+    }
+  }
   // B operands of the scores: row m0 + 32 mh + l32, coordinates 64 hi + 8 ks .. + 7 of q~
   const int mrow = m0 + 32 * mh + l32;
   const bool row_live = mrow < rows_total;
   bf16x8 qb_h[8], qb_l[8];
-  {
-    const float *qp = a.ws_qprep + (static_cast<int64_t>(row_id) * rows_total + (row_live ? mrow : 0)) * kQpStride + 64 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-      if (row_live) {
-        x0 = *reinterpret_cast<const float4 *>(qp + 8 * ks);
-        x1 = *reinterpret_cast<const float4 *>(qp + 8 * ks + 4);
-      }
-      uint32_t h[4], l[4];
-      split_pair(x0.x, x0.y, h[0], l[0]);
-      split_pair(x0.z, x0.w, h[1], l[1]);
-      split_pair(x1.x, x1.y, h[2], l[2]);
-      split_pair(x1.z, x1.w, h[3], l[3]);
-      qb_h[ks] = as_bf16x8(h[0], h[1], h[2], h[3]);
-      qb_l[ks] = as_bf16x8(l[0], l[1], l[2], l[3]);
-    }
+  for (int ks = 0; ks < 8; ++ks) {
+    const int qo = (32 * mh + l32) * kSStride + 64 * hi + 8 * ks;
+    qb_h[ks] = *reinterpret_cast<const bf16x8 *>(&sm.u.loop.qh[qo]);
+    qb_l[ks] = *reinterpret_cast<const bf16x8 *>(&sm.u.loop.ql[qo]);
   }
   __syncthreads();
 
@@ -612,33 +626,18 @@ DecodePlan plan_chunk_mfma(int batch, int n_q_heads, int n_kv_heads, int n_new, 
   p.off_qslot = 0;
   p.off_part_o = 0;
   p.off_part_ml = align(p.off_part_o + static_cast<size_t>(groups) * g * D * sizeof(float));
-  p.off_qprep = align(p.off_part_ml + static_cast<size_t>(groups) * g * 2 * sizeof(float));
-  p.total_bytes = align(p.off_qprep + static_cast<size_t>(qrows) * g * kQpStride * sizeof(float));
+  p.total_bytes = align(p.off_part_ml + static_cast<size_t>(groups) * g * 2 * sizeof(float));
   return p;
 }
 
 hipError_t launch_chunk_mfma(const DecodeArgs &a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
   const int n_mb = (g * a.n_new + kRows - 1) / kRows;
-  if (a.n_chunks > kMaxDecodeChunks || a.v_bits < 1 || a.v_bits > 4 || a.n_new < 1 ||
-      static_cast<int64_t>(a.n_kv_heads) * n_mb > 65535 || a.ws_qprep == nullptr)
+  if (a.n_chunks > kMaxDecodeChunks || a.v_bits < 1 || a.v_bits > 4 || a.n_new < 1 || g < 1 || g > 8 || a.k_split ||
+      static_cast<int64_t>(a.n_kv_heads) * n_mb > 65535 || a.k_frag_rot == nullptr ||
+      (a.qjl_m > 0 && a.k_frag_qjl == nullptr))
     return hipErrorInvalidValue;
-  const int n_qrows = a.batch * a.n_kv_heads * a.n_new;   // (b, kv head, j)
-  const bool qjl = a.qjl_m > 0;
-  switch (g) {
-#define TQ_QP(GG)                                                                                   \
-  case GG:                                                                                          \
-    if (qjl)                                                                                        \
-      hipLaunchKernelGGL((qprep_kernel<true, GG>), dim3(n_qrows), dim3(kQpThreads), 0, stream, a);  \
-    else                                                                                            \
-      hipLaunchKernelGGL((qprep_kernel<false, GG>), dim3(n_qrows), dim3(kQpThreads), 0, stream, a); \
-    break;
-    TQ_QP(1) TQ_QP(2) TQ_QP(4) TQ_QP(8)
-#undef TQ_QP
-    default: return hipErrorInvalidValue;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   const dim3 grid(a.n_chunks, a.n_kv_heads * n_mb, a.batch);
   switch (a.k_bits) {
     case 1: e = launch_tiles<1>(a, grid, stream); break;

@@ -1105,7 +1105,6 @@ DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int64_t t_cap) 
   p.off_qslot = 0;
   p.off_part_o = align(p.off_qslot + static_cast<size_t>(groups) * g * D * sizeof(float));
   p.off_part_ml = align(p.off_part_o + static_cast<size_t>(groups) * g * D * sizeof(float));
-  p.off_qprep = 0;
   p.total_bytes = align(p.off_part_ml + static_cast<size_t>(groups) * g * 2 * sizeof(float));
   return p;
 }

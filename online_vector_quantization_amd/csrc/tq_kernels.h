@@ -111,7 +111,6 @@ struct DecodePlan {
   size_t off_qslot;        // bytes into the workspace: float[groups][d][g], q~ per work-group (coordinate-major)
   size_t off_part_o;       // float[groups][g][d]: rotated partial outputs
   size_t off_part_ml;      // float[groups][g][2]: running max and sum
-  size_t off_qprep;        // chunk attention on the matrix cores: float[B*Hq*n_new][2d], (q~, s) per query
   size_t total_bytes;
 };
 
@@ -149,6 +148,8 @@ struct DecodeArgs {
   float *scores;           // float[B][Hq][t_cap] scaled logits of t < T; optional for attention, the output of the logits-only kernel
   const float *rot_k_t;    // Pi_k^T row-major (d x d): entry [i][j] = Pi_k[j][i]
   const float *qjl_rot_t;  // (S Pi_k)^T row-major (d x m): s = S Pi_k q in one product
+  const uint4 *k_frag_rot; // chunk attention: bf16 hi/lo operand fragments of Pi_k (the encode's layout)
+  const uint4 *k_frag_qjl; // and of -S (keys with QJL)
   const float *rot_v;      // Pi_v row-major (d x d)
   const float *k_lut;      // key dequantization table (kKeyLutBytes)
   const float *v_lut;      // value pair table (kPairLutBytes)
@@ -163,7 +164,6 @@ struct DecodeArgs {
   float *ws_qslot;
   float *ws_part_o;        // [B*Hkv][n_chunks][g][d]: rotated back (decode kernel) or rotated (chunk kernel)
   float *ws_part_ml;       // [B*Hkv][n_chunks][g][2]
-  float *ws_qprep;         // chunk attention on the matrix cores: (q~, s) per query row
   int chunk, n_chunks;
 };
 
