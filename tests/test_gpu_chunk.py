@@ -201,3 +201,31 @@ def test_chunk_decode_kernel_wide_batch():
     _log(f"  vs oracle: max-abs {err:.2e}")
     assert err <= 2e-3, f"max-abs error {err:.3e}"
     assert np.all(g_np[0, :, :n_new - 3] == 0.0)
+
+
+@pytest.mark.parametrize("qdt", ["bf16", "f32"])
+def test_chunk_mfma_query_4byte_aligned(qdt):
+    """The matrix-core path reads the queries in its own prologue; the call
+    promises only 4-byte alignment of q, so a query tensor starting 4 bytes
+    past a 16-byte boundary must give the same result, bit for bit, as an
+    aligned copy of it."""
+    B, Hkv, g, n_new, t_cap = 2, 2, 4, 8, 600
+    rng = np.random.default_rng(77)
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap))
+    v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t_cap))
+    qf = rng.standard_normal((B, Hkv * g, n_new, 128)).astype(np.float32)
+    q = H.to_device(synth.bf16_bits(qf), "bf16") if qdt == "bf16" else H.to_device(qf, "f32")
+    assert T.api.chunk_uses_mfma(g, n_new)
+    kcb, vcb = H.gpu_book(2, 128), H.gpu_book(3, 0)
+    kc, vc = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, t_cap, t_cap)
+    sl = torch.tensor([600, 333], dtype=torch.int32, device=H.DEV)
+    shift = 4 // q.element_size()
+    buf = torch.empty(q.numel() + shift, dtype=q.dtype, device=H.DEV)
+    q_off = buf[shift:].view(q.shape)
+    q_off.copy_(q)
+    assert q_off.data_ptr() % 16 == 4
+    _log(f"chunk, query at a 4-byte offset: q={qdt}")
+    a = T.chunk_attention(kcb, vcb, q, kc, vc, sl)
+    b = T.chunk_attention(kcb, vcb, q_off, kc, vc, sl)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
