@@ -374,16 +374,15 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   const int t_begin = chunk_id * a.chunk;
   const int t_end = min(T, t_begin + a.chunk);
 
-  // The wave's first tile is requested before the prologue, whose work then
-  // hides its memory latency.
   Tile<KB, VB, QJL, SC, SPL> ta{};
   const int t0 = t_begin + wave * kTile;
-  if (t0 < t_end) load_tile<3, KB, VB, QJL, SC, SPL>(a, row0, t0, n, kq, lo_col, ta);
 
   // ------------------------------------------------------------ prologue
   // Striped copies of the codebooks' tables (key code pairs -> fp16 (hi, lo)
   // of 256 c per code, pairs of tokens' value codes -> bf16 (hi, lo) of c per
-  // token, sign bytes -> eight fp16 +-1).
+  // token, sign bytes -> eight fp16 +-1).  The tables sit in L2; they are
+  // filled before the wave's first tile is requested, since a wait for one
+  // load also waits for every load issued before it.
   {
     auto fill_pairs = [&](unsigned char *dst, const void *src, int entries) {
       const uint2 *t = reinterpret_cast<const uint2 *>(src);
@@ -406,8 +405,9 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   }
   // q~ = Pi_k q and s = (S Pi_k) q of the g heads in fp32: thread (i, part)
   // forms the partial dot products over input coordinates 32 part .. + 31 of
-  // column i of Pi_k^T and of (S Pi_k)^T (every global read issued first),
-  // summed over the four parts in LDS.
+  // column i of Pi_k^T and of (S Pi_k)^T, summed over the four parts in LDS.
+  // Those columns and the queries are requested first, then the wave's first
+  // tile, whose HBM latency the products hide.
   {
     const int pi_ = tid & (D - 1), part = tid >> 7;
     const bool in_pro = part < 4;   // wave-uniform: the first 512 threads
@@ -420,10 +420,21 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
         for (int jj = 0; jj < 32; ++jj) sv[jj] = a.qjl_rot_t[(32 * part + jj) * kQjlDim + pi_];
       }
     }
-    for (int e = tid; e < 8 * D; e += kThreads)
-      sm.u.pro.q[e / D][e % D] =
-          (e / D < G) ? load_query(a.q, a.q_bf16, (static_cast<int64_t>(b) * a.n_q_heads + hk * G + e / D) * D + e % D)
-                      : 0.f;
+    constexpr int kQPer = (8 * D + kThreads - 1) / kThreads;
+    float qv[kQPer];
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int e = tid + k * kThreads;
+      qv[k] = (e < 8 * D && e / D < G)
+                  ? load_query(a.q, a.q_bf16, (static_cast<int64_t>(b) * a.n_q_heads + hk * G + e / D) * D + e % D)
+                  : 0.f;
+    }
+    if (t0 < t_end) load_tile<3, KB, VB, QJL, SC, SPL>(a, row0, t0, n, kq, lo_col, ta);
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int e = tid + k * kThreads;
+      if (e < 8 * D) sm.u.pro.q[e / D][e % D] = qv[k];
+    }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
@@ -825,16 +836,18 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (in_inv) {
-    float r[8];
+    // heads outermost: one uniform branch per head, its 32 LDS reads issued
+    // together (a head test inside the coordinate loop became one branch and
+    // one LDS round trip per product)
 #pragma unroll
-    for (int h = 0; h < 8; ++h) r[h] = 0.f;
+    for (int h = 0; h < 8; ++h) {
+      if (h < G) {
+        float r = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj)
-#pragma unroll
-      for (int h = 0; h < 8; ++h)
-        if (h < G) r[h] = fmaf(pvr[jj], sm.u.inv.ot[h][32 * q4 + jj], r[h]);
-#pragma unroll
-    for (int h = 0; h < 8; ++h) sm.u.inv.red[q4][h][i4] = r[h];
+        for (int jj = 0; jj < 32; ++jj) r = fmaf(pvr[jj], sm.u.inv.ot[h][32 * q4 + jj], r);
+        sm.u.inv.red[q4][h][i4] = r;
+      }
+    }
   }
   __syncthreads();
   // the chunk's (max, sum) per head, max in natural-log units (the merge's)
