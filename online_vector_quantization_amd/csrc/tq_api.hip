@@ -153,6 +153,10 @@ tq_status upload_tables(tq_codebook *cb) {
   off = align256(off + tq::kFragBytes);
   cb->off_qjl_frag = off;
   off = align256(off + (m > 0 ? tq::kFragBytes : 0));
+  cb->off_dec_rot_frag = off;
+  off = align256(off + tq::kFragBytes);
+  cb->off_dec_qjl_frag = off;
+  off = align256(off + (m > 0 ? tq::kFragBytes : 0));
   cb->off_rot_f32 = off;
   off = align256(off + static_cast<size_t>(d) * d * sizeof(float));
   cb->off_rot_t_f32 = off;
@@ -194,17 +198,26 @@ tq_status upload_tables(tq_codebook *cb) {
   float *rt = reinterpret_cast<float *>(img.data() + cb->off_rot_t_f32);
   for (int i = 0; i < d; ++i)
     for (int j = 0; j < d; ++j) rt[i * d + j] = h.rotation[static_cast<size_t>(j) * d + i];
+  // the matrix-core decode's query operands: Pi (its rows in the encode's
+  // coordinate order) and S Pi, in fp16 hi/lo
+  if (!tq::pack_decode_fragments(h.rotation64.data(), img.data() + cb->off_dec_rot_frag, split))
+    return fail(TQ_ERR_UNSUPPORTED, "rotation entry out of the decode operands' fp16 range");
   if (m > 0) {
-    // (S Pi)^T in double, rounded once: the decode projects the raw query
+    // S Pi in double, rounded once per use: the decode projects the raw query
     // with it (s = S Pi q) instead of projecting Pi q with S.
-    float *st = reinterpret_cast<float *>(img.data() + cb->off_qjl_rot_t_f32);
-    for (int i = 0; i < d; ++i)
-      for (int r = 0; r < m; ++r) {
+    std::vector<double> sp(static_cast<size_t>(m) * d);
+    for (int r = 0; r < m; ++r)
+      for (int i = 0; i < d; ++i) {
         double v = 0.0;
         for (int j = 0; j < d; ++j)
           v += h.qjl64[static_cast<size_t>(r) * d + j] * h.rotation64[static_cast<size_t>(j) * d + i];
-        st[i * m + r] = static_cast<float>(v);
+        sp[static_cast<size_t>(r) * d + i] = v;
       }
+    float *st = reinterpret_cast<float *>(img.data() + cb->off_qjl_rot_t_f32);
+    for (int i = 0; i < d; ++i)
+      for (int r = 0; r < m; ++r) st[i * m + r] = static_cast<float>(sp[static_cast<size_t>(r) * d + i]);
+    if (!tq::pack_decode_fragments(sp.data(), img.data() + cb->off_dec_qjl_frag, false))
+      return fail(TQ_ERR_UNSUPPORTED, "S Pi entry out of the decode operands' fp16 range");
   }
   auto pair = [](uint16_t x, uint16_t y) { return static_cast<uint32_t>(x) | (static_cast<uint32_t>(y) << 16); };
   // Matrix-core decode operand tables of one codebook (layouts in
@@ -546,6 +559,8 @@ tq_status prepare_keys(const tq_codebook *kcb, const void *q, tq_dtype q_dtype, 
   a.qjl_rot_t = m > 0 ? dev_ptr<float>(kcb, kcb->off_qjl_rot_t_f32) : nullptr;
   a.k_frag_rot = dev_ptr<uint4>(kcb, kcb->off_rot_frag);
   a.k_frag_qjl = m > 0 ? dev_ptr<uint4>(kcb, kcb->off_qjl_frag) : nullptr;
+  a.k_dfrag_rot = dev_ptr<uint4>(kcb, kcb->off_dec_rot_frag);
+  a.k_dfrag_qjl = m > 0 ? dev_ptr<uint4>(kcb, kcb->off_dec_qjl_frag) : nullptr;
   a.k_lut = dev_ptr<float>(kcb, kcb->off_key_lut);
   a.k_pair = dev_ptr<float>(kcb, kcb->off_pair_lut);
   a.mk_lut = dev_ptr<void>(kcb, kcb->off_mkey_lut);

@@ -52,6 +52,8 @@ struct tq_codebook {
   size_t off_thresholds = 0;      // float[L-1] (padded)
   size_t off_rot_frag = 0;        // encode A-operand fragments of Pi: hi then lo
   size_t off_qjl_frag = 0;        // encode A-operand fragments of S: hi then lo
+  size_t off_dec_rot_frag = 0;    // decode fp16 fragments of 2^kDecFragExp Pi: hi then lo
+  size_t off_dec_qjl_frag = 0;    // decode fp16 fragments of 2^kDecFragExp S Pi: hi then lo
   size_t off_rot_f32 = 0;         // float[d*d] row-major Pi
   size_t off_rot_t_f32 = 0;       // float[d*d] row-major Pi^T
   size_t off_qjl_rot_t_f32 = 0;   // float[d*m] row-major (S Pi)^T

@@ -69,6 +69,16 @@ struct EncodeArgs {
 // -mat (the QJL matrix: the encode then reads -p, whose sign bit is the sketch).
 void pack_encode_fragments(const float *mat, void *dst, bool split_rows, bool split_cols, bool negate);
 
+// The matrix-core decode's query products take fp16 operands: the fragments
+// hold fp16 hi and lo of 2^kDecFragExp * mat (128 x 128, row-major, entries
+// of magnitude below 2^7 so that the scaled hi part stays finite), with lo
+// the rounding of the remainder (22 significant bits in all), in the layout of
+// pack_encode_fragments.  split_rows as there; the inputs are the query's
+// coordinates in natural order.
+constexpr int kDecFragExp = 8;
+// False if an entry is too large for the scaled fp16 parts.
+bool pack_decode_fragments(const double *mat, void *dst, bool split_rows);
+
 // Builds the quantizer cell table (4 floats per cell); false if the
 // thresholds do not fit the cell grid (then the GPU path is unsupported).
 bool build_quant_cells(const float *thresholds, const float *centroids, int levels, float *cells,
@@ -150,6 +160,8 @@ struct DecodeArgs {
   const float *qjl_rot_t;  // (S Pi_k)^T row-major (d x m): s = S Pi_k q in one product
   const uint4 *k_frag_rot; // chunk attention: bf16 hi/lo operand fragments of Pi_k (the encode's layout)
   const uint4 *k_frag_qjl; // and of -S (keys with QJL)
+  const uint4 *k_dfrag_rot; // matrix-core decode: fp16 hi/lo fragments of 2^kDecFragExp Pi_k
+  const uint4 *k_dfrag_qjl; // and of 2^kDecFragExp S Pi_k (keys with QJL)
   const float *rot_v;      // Pi_v row-major (d x d)
   const float *k_lut;      // key dequantization table (kKeyLutBytes)
   const float *v_lut;      // value pair table (kPairLutBytes)

@@ -334,9 +334,13 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
     alignas(16) unsigned char stab[QJL ? 256 * SignTab::kRow : 16];
     union {
       struct {
-        float q[8][D];                 // the g queries
-        float part[4][8][D];           // partial dot products of q~
-        float part_s[QJL ? 4 : 1][8][D];   // and of s
+        // fp16 hi / lo of the g scaled queries, [head][coordinate]: the B
+        // operands of the prologue's products (rows of D + 8: the 8 heads'
+        // 16-byte reads of one k-step spread over the banks), and each head's
+        // power of two
+        alignas(16) uint16_t xh[8][D + 8];
+        alignas(16) uint16_t xl[8][D + 8];
+        int xexp[8];
         float qt[8][D];                // q~ (scaled), [head][coordinate]
         float st[8][D];                // s (scaled)
         int fexp[8][2];                // per head: the fp16 operands' power-of-two scales
@@ -403,68 +407,93 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
             st[i / SignTab::kCopies];
     }
   }
-  // q~ = Pi_k q and s = (S Pi_k) q of the g heads in fp32: thread (i, part)
-  // forms the partial dot products over input coordinates 32 part .. + 31 of
-  // column i of Pi_k^T and of (S Pi_k)^T, summed over the four parts in LDS.
-  // Those columns and the queries are requested first, then the wave's first
-  // tile, whose HBM latency the products hide.
+  // q~ = Pi_k q and s = S Pi_k q of the g heads on the matrix cores
+  // (v_mfma_f32_16x16x32_f16), from the codebook's fp16 hi/lo fragments of
+  // 2^kDecFragExp Pi_k and 2^kDecFragExp S Pi_k in the encode's layout: wave
+  // t takes output block t of both, whose lane (n, kq) receives coordinate
+  // enc_coord(kq, t, e) of q~ (32 kq + 4 t + e of s) for head n (B columns
+  // 8..15 are zero).  B element e of k-step ks is query coordinate 32 kq +
+  // 8 ks + e, as fp16 hi/lo of 2^xe q with a per-head power of two xe that
+  // brings the largest |q| into [64, 128) (a bf16 query has no lo part).  The
+  // passes hi*hi + lo*hi (+ hi*lo for fp32 queries) keep 22 significant bits
+  // of either operand.  The fragments and the queries are requested first,
+  // then the wave's first tile, whose HBM latency the products hide.
   {
-    const int pi_ = tid & (D - 1), part = tid >> 7;
-    const bool in_pro = part < 4;   // wave-uniform: the first 512 threads
-    float pv[32], sv[QJL ? 32 : 1];
-    if (in_pro) {
+    const bool in_mm = wave < 8;   // wave-uniform: wave h < 8 also reads head h's query
+    f16x8 ph[4], pl[4], fsh[QJL ? 4 : 1], fsl[QJL ? 4 : 1];
+    float q0 = 0.f, q1 = 0.f;
+    if (in_mm) {
+      const uint4 *fr = a.k_dfrag_rot;
 #pragma unroll
-      for (int jj = 0; jj < 32; ++jj) pv[jj] = a.rot_k_t[(32 * part + jj) * D + pi_];
-      if constexpr (QJL) {
-#pragma unroll
-        for (int jj = 0; jj < 32; ++jj) sv[jj] = a.qjl_rot_t[(32 * part + jj) * kQjlDim + pi_];
+      for (int ks = 0; ks < 4; ++ks) {
+        ph[ks] = __builtin_bit_cast(f16x8, fr[((0 * 8 + wave) * 4 + ks) * 64 + lane]);
+        pl[ks] = __builtin_bit_cast(f16x8, fr[((1 * 8 + wave) * 4 + ks) * 64 + lane]);
       }
-    }
-    constexpr int kQPer = (8 * D + kThreads - 1) / kThreads;
-    float qv[kQPer];
+      if constexpr (QJL) {
+        const uint4 *fq = a.k_dfrag_qjl;
 #pragma unroll
-    for (int k = 0; k < kQPer; ++k) {
-      const int e = tid + k * kThreads;
-      qv[k] = (e < 8 * D && e / D < G)
-                  ? load_query(a.q, a.q_bf16, (static_cast<int64_t>(b) * a.n_q_heads + hk * G + e / D) * D + e % D)
-                  : 0.f;
+        for (int ks = 0; ks < 4; ++ks) {
+          fsh[ks] = __builtin_bit_cast(f16x8, fq[((0 * 8 + wave) * 4 + ks) * 64 + lane]);
+          fsl[ks] = __builtin_bit_cast(f16x8, fq[((1 * 8 + wave) * 4 + ks) * 64 + lane]);
+        }
+      }
+      if (wave < G) {   // lane l: coordinates 2 l, 2 l + 1
+        const int64_t qi = (static_cast<int64_t>(b) * a.n_q_heads + hk * G + wave) * D + 2 * lane;
+        q0 = load_query(a.q, a.q_bf16, qi);
+        q1 = load_query(a.q, a.q_bf16, qi + 1);
+      }
     }
     if (t0 < t_end) load_tile<3, KB, VB, QJL, SC, SPL>(a, row0, t0, n, kq, lo_col, ta);
+    if (in_mm) {
+      float mx = fmaxf(fabsf(q0), fabsf(q1));
 #pragma unroll
-    for (int k = 0; k < kQPer; ++k) {
-      const int e = tid + k * kThreads;
-      if (e < 8 * D) sm.u.pro.q[e / D][e % D] = qv[k];
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      int ex = 0;
+      (void)frexpf(mx, &ex);
+      const int xe = (mx > 0.f && mx < INFINITY) ? 7 - ex : 0;
+      const float y0 = ldexpf(q0, xe), y1 = ldexpf(q1, xe);
+      *reinterpret_cast<uint32_t *>(&sm.u.pro.xh[wave][2 * lane]) = split_f16(y0, y1, false);
+      *reinterpret_cast<uint32_t *>(&sm.u.pro.xl[wave][2 * lane]) = split_f16(y0, y1, true);
+      if (lane == 0) sm.u.pro.xexp[wave] = xe;
     }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      if (in_pro && h < G) {
-        float aq = 0.f, as = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 32; ++jj) {
-          const float qj = sm.u.pro.q[h][32 * part + jj];
-          aq = fmaf(pv[jj], qj, aq);
-          if constexpr (QJL) as = fmaf(sv[jj], qj, as);
-        }
-        sm.u.pro.part[part][h][pi_] = aq;
-        if constexpr (QJL) sm.u.pro.part_s[part][h][pi_] = as;
-      }
+    if constexpr (!QJL) {
+      for (int e = tid; e < 8 * D; e += kThreads) sm.u.pro.st[e / D][e % D] = 0.f;
     }
     __syncthreads();
     // scaled by scale * log2 e (the sign term also by sqrt(pi/2)/m); heads past g are zero
     const float qsc = a.scale * kLog2e, ssc = a.scale * kLog2e * a.qjl_coef;
-    for (int e = tid; e < 8 * D; e += kThreads) {
-      const int h = e / D, i = e % D;
-      float v = 0.f, w = 0.f;
-      if (h < G) {
+    if (in_mm) {
+      const bool q_f32 = a.q_bf16 == 0;
+      const f16x8 zero8 = as_f16x8(0u, 0u, 0u, 0u);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acs = acc;
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          v += sm.u.pro.part[pp][h][i];
-          if constexpr (QJL) w += sm.u.pro.part_s[pp][h][i];
+      for (int ks = 0; ks < 4; ++ks) {
+        const int xo = 32 * kq + 8 * ks;
+        const f16x8 bh = lo_col ? zero8 : *reinterpret_cast<const f16x8 *>(&sm.u.pro.xh[hcol][xo]);
+        acc = mfma_f16(ph[ks], bh, acc);
+        acc = mfma_f16(pl[ks], bh, acc);
+        if constexpr (QJL) {
+          acs = mfma_f16(fsh[ks], bh, acs);
+          acs = mfma_f16(fsl[ks], bh, acs);
+        }
+        if (q_f32) {
+          const f16x8 bl = lo_col ? zero8 : *reinterpret_cast<const f16x8 *>(&sm.u.pro.xl[hcol][xo]);
+          acc = mfma_f16(ph[ks], bl, acc);
+          if constexpr (QJL) acs = mfma_f16(fsh[ks], bl, acs);
         }
       }
-      sm.u.pro.qt[h][i] = v * qsc;
-      sm.u.pro.st[h][i] = w * ssc;
+      if (!lo_col) {
+        const bool live = hcol < G;
+        const float un = ldexpf(1.f, -(kDecFragExp + sm.u.pro.xexp[hcol]));   // the operands' scales
+        const float kq_ = un * qsc, ks_ = un * ssc;
+        const int c = enc_coord(SPL, kq, wave, 0);   // q~ coordinates c .. c + 3
+        *reinterpret_cast<float4 *>(&sm.u.pro.qt[hcol][c]) =
+            live ? make_float4(acc[0] * kq_, acc[1] * kq_, acc[2] * kq_, acc[3] * kq_) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (QJL) {
+          *reinterpret_cast<float4 *>(&sm.u.pro.st[hcol][32 * kq + 4 * wave]) =
+              live ? make_float4(acs[0] * ks_, acs[1] * ks_, acs[2] * ks_, acs[3] * ks_) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
     }
     __syncthreads();
     // per head, a power of two that brings the largest |q~| (and |s|) into
@@ -921,7 +950,7 @@ hipError_t launch_k(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
 hipError_t launch_mdecode_main(const DecodeArgs &a, bool scores_only, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
   if (!mdecode_can_run(a) || a.n_chunks > kMaxDecodeChunks || g < 1 || g > 8 || a.n_kv_heads > 65535 ||
-      a.mk_lut == nullptr || a.rot_k_t == nullptr || (a.qjl_m > 0 && (a.qjl_rot_t == nullptr || a.sg_lut == nullptr)) ||
+      a.mk_lut == nullptr || a.k_dfrag_rot == nullptr || (a.qjl_m > 0 && (a.k_dfrag_qjl == nullptr || a.sg_lut == nullptr)) ||
       (!scores_only && a.mv_lut == nullptr) || (a.k_split && a.mk_lut_w == nullptr) ||
       (!scores_only && (a.v_split != a.k_split || (a.v_split && a.mv_lut_w == nullptr))))
     return hipErrorInvalidValue;
@@ -942,6 +971,31 @@ hipError_t launch_mdecode_main(const DecodeArgs &a, bool scores_only, hipStream_
     case 4: return scores_only ? launch_k<4, true, false>(a, grid, stream) : launch_k<4, false, false>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool pack_decode_fragments(const double *mat, void *dst, bool split_rows) {
+  // Element (t, s, lane, e) as in pack_encode_fragments: lane % 16 picks output
+  // row enc_coord(i / 4, t, i % 4), element e with lane / 16 picks input
+  // column 32 (lane / 16) + 8 s + e.
+  const double sc = static_cast<double>(1 << kDecFragExp);
+  uint16_t *out = static_cast<uint16_t *>(dst);
+  for (int i = 0; i < kHeadDim * kHeadDim; ++i)
+    if (!(std::fabs(mat[i]) < 128.0)) return false;
+  for (int t = 0; t < 8; ++t)
+    for (int s = 0; s < 4; ++s)
+      for (int lane = 0; lane < 64; ++lane)
+        for (int e = 0; e < 8; ++e) {
+          const int i = lane & 15, kq = lane >> 4;
+          const int row = enc_coord(split_rows, i >> 2, t, i & 3);
+          const int col = 32 * kq + 8 * s + e;
+          const double v = sc * mat[row * kHeadDim + col];
+          const _Float16 hi = static_cast<_Float16>(static_cast<float>(v));
+          const _Float16 lo = static_cast<_Float16>(static_cast<float>(v - static_cast<double>(hi)));
+          const size_t at = (((static_cast<size_t>(t) * 4 + s) * 64 + lane) * 8) + e;
+          out[at] = __builtin_bit_cast(uint16_t, hi);
+          out[kFragBytesPerSplit / 2 + at] = __builtin_bit_cast(uint16_t, lo);
+        }
+  return true;
 }
 
 }  // namespace tq
