@@ -321,13 +321,20 @@ __device__ __forceinline__ uint32_t bits_at(uint32_t lo, uint32_t hi, int bit) {
 
 template <int KB, int VB, bool QJL, bool SC, bool SPL>
 __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
-  constexpr int kKeyEntries = 1 << (2 * KB);
+  // 1- and 2-bit key codes (uniform widths, with the value sum): one 16-byte
+  // lookup per k-step, a table of code quads (four coordinates' (hi, lo)
+  // operands); otherwise two lookups per k-step into the table of code pairs
+  // (the scores-only kernel keeps the smaller table: two work-groups per CU)
+  constexpr bool kQuad = KB <= 2 && !SPL && !SC;
+  constexpr int kKeyEntries = kQuad ? 1 : 1 << (2 * KB);
+  constexpr int kQuadEntries = kQuad ? 1 << (4 * KB) : 1;
   constexpr int kValEntries = SC ? 1 : 1 << (2 * VB);
   // split widths: the wide codebooks' tables (b' + 1 bits)
   constexpr int kKeyEntriesW = SPL ? 1 << (2 * KB + 2) : 1;
   constexpr int kValEntriesW = (SPL && !SC) ? 1 << (2 * VB + 2) : 1;
   struct Smem {
     alignas(16) unsigned char ktab[kKeyEntries * PairTab::kRow];
+    alignas(16) unsigned char qtab[kQuadEntries * SignTab::kRow];
     alignas(16) unsigned char vtab[kValEntries * PairTab::kRow];
     alignas(16) unsigned char ktab_w[kKeyEntriesW * PairTab::kRow];
     alignas(16) unsigned char vtab_w[kValEntriesW * PairTab::kRow];
@@ -394,7 +401,19 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
         *reinterpret_cast<uint2 *>(dst + (i / PairTab::kCopies) * PairTab::kRow + (i % PairTab::kCopies) * 8) =
             t[i / PairTab::kCopies];
     };
-    fill_pairs(sm.ktab, a.mk_lut, kKeyEntries);
+    if constexpr (kQuad) {
+      // quad q = codes (q & m, q >> 2 KB): the pair entries of its two halves
+      const uint2 *t = reinterpret_cast<const uint2 *>(a.mk_lut);
+      constexpr int kPairMask = (1 << (2 * KB)) - 1;
+      for (int i = tid; i < kQuadEntries * SignTab::kCopies; i += kThreads) {
+        const int q = i / SignTab::kCopies;
+        const uint2 lo = t[q & kPairMask], hi = t[q >> (2 * KB)];
+        *reinterpret_cast<uint4 *>(sm.qtab + q * SignTab::kRow + (i % SignTab::kCopies) * 16) =
+            make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    } else {
+      fill_pairs(sm.ktab, a.mk_lut, kKeyEntries);
+    }
     if constexpr (SPL) fill_pairs(sm.ktab_w, a.mk_lut_w, kKeyEntriesW);
     if constexpr (!SC) {
       fill_pairs(sm.vtab, a.mv_lut, kValEntries);
@@ -593,6 +612,15 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
+        if constexpr (kQuad) {
+          // quad s: bits [4 KB s, 4 KB s + 4 KB) of the lane's codes (within one word)
+          constexpr int kBits = 4 * KB;
+          const int bit = kBits * s, w = bit >> 5, sh = bit & 31;
+          const uint32_t idx = (cur.kc[hf][w] >> sh) & ((1u << kBits) - 1u);
+          const uint4 e = *reinterpret_cast<const uint4 *>(sm.qtab + (idx << SignTab::kShift) + lane_s);
+          sacc[hf] = mfma_f16(as_f16x8(e.x, e.y, e.z, e.w), qop[s], sacc[hf]);
+          continue;
+        }
         uint32_t ka[2];
         const bool wide = SPL && s < 4;
 #pragma unroll

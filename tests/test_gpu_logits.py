@@ -122,3 +122,31 @@ def test_logits_batched_full():
                           H.oracle_book(1, 128), 4)
     worst = H.check_logits(got.cpu().numpy(), ref, lens)
     _log(f"  worst relative error {worst:.2e}")
+
+
+@pytest.mark.parametrize("kbits,g,qdt", [(2, 8, "bf16"), (3, 8, "f32"), (3, 4, "bf16"), (4, 8, "bf16"), (2, 4, "f32")])
+def test_logits_precision_margin(kbits, g, qdt):
+    """The query products keep fp32-level precision on both decode kernels
+    (the matrix cores at g = 8 and at g = 4 with 3-bit codes, the vector ALU at
+    g = 4 with 2-bit codes): worst relative logit error at most 2e-6, fifty
+    times inside the 1e-4 bar.  Observed 3e-7 .. 5e-7; products with 16-bit
+    (bf16 hi/lo) operands give 4.5e-6 .. 1e-5 here."""
+    B, Hkv, t = 2, 2, 1536
+    Hq = Hkv * g
+    rng = np.random.default_rng(7 + kbits + g)
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t, lognormal_sigma=0.5))
+    qf = rng.standard_normal((B, Hq, 128)).astype(np.float32) * 3
+    q = H.to_device(synth.bf16_bits(qf), "bf16") if qdt == "bf16" else H.to_device(qf, "f32")
+    kcb = H.gpu_book(kbits, 128)
+    kc = T.CompressedCache.allocate(kcb, B, Hkv, t)
+    T.encode_into_cache(kcb, H.to_device(k.reshape(-1, 128), "bf16"), kc)
+    lens = [t, t - 100]
+    sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+    _log(f"logits precision kbits={kbits} g={g} q={qdt}")
+    got = T.attention_logits(kcb, q, kc, sl, logits=_nan_logits(B, Hq, t))
+    torch.cuda.synchronize()
+    ref = H.oracle_logits(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), lens,
+                          H.oracle_book(kbits, 128), g)
+    worst = H.check_logits(got.cpu().numpy(), ref, lens)
+    _log(f"  worst relative error {worst:.2e}")
+    assert worst <= 2e-6, f"relative logit error {worst:.3e}"
