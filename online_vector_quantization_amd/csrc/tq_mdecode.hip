@@ -814,16 +814,26 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
     // i + 2's keys load into the free halves.  Loads past the row's end read
     // its last token (in bounds); their scores are masked to -inf, and the
     // last step scores one such tile that nothing uses.
+    //
+    // Waves w and w + 4 share a SIMD, whose scheduler issues the older wave
+    // first: left alone, one of them finishes its tiles long before the other,
+    // which then runs its last tiles with no partner to overlap.  Each wave
+    // therefore raises its priority on every other tile, the two in opposite
+    // phase, so that they take turns.  (Tiles stay statically assigned, so the
+    // result does not depend on the timing.)
     load_tile<1, KB, VB, QJL, SC, SPL>(a, row0, t0 + kStride, n, kq, lo_col, tn);
     float la[4], lb[4];
     score_tile(ta, t0, la);
+    int turn = wave >> 2;
     for (int tt = t0;;) {
+      if (++turn & 1) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
       load_tile<2, KB, VB, QJL, SC, SPL>(a, row0, tt + kStride, n, kq, lo_col, tn);
       load_tile<1, KB, VB, QJL, SC, SPL>(a, row0, tt + 2 * kStride, n, kq, lo_col, ta);
       value_tile(ta, la, tt);
       score_tile(tn, tt + kStride, lb);
       tt += kStride;
       if (tt >= t_end) break;
+      if (++turn & 1) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
       load_tile<2, KB, VB, QJL, SC, SPL>(a, row0, tt + kStride, n, kq, lo_col, ta);
       load_tile<1, KB, VB, QJL, SC, SPL>(a, row0, tt + 2 * kStride, n, kq, lo_col, tn);
       value_tile(tn, lb, tt);
@@ -834,6 +844,7 @@ __global__ __launch_bounds__(kThreads) void mdecode_kernel(DecodeArgs a) {
   }
 
   if constexpr (SC) return;   // uniform: no barrier follows for any thread
+  __builtin_amdgcn_s_setprio(0);
 
   // ------------------------------------------------------------ merge waves
   // Pi_v^T of the chunk's sum: thread (i4, q4) applies rows 32 q4 .. + 31 of
