@@ -150,3 +150,31 @@ def test_logits_precision_margin(kbits, g, qdt):
     worst = H.check_logits(got.cpu().numpy(), ref, lens)
     _log(f"  worst relative error {worst:.2e}")
     assert worst <= 2e-6, f"relative logit error {worst:.3e}"
+
+
+@pytest.mark.parametrize("exp2,qdt", [(-60, "bf16"), (60, "bf16"), (-40, "f32"), (40, "f32")])
+def test_logits_query_magnitude_extremes(exp2, qdt):
+    """The matrix-core decode scales each head's query by a power of two into
+    fp16 range before its products: queries 2^+-60 (bf16) and 2^+-40 (fp32)
+    give the oracle's logits to the same relative bar, with no overflow or
+    flush to zero (g = 8, 2-bit codes + QJL)."""
+    B, Hkv, g, t = 1, 2, 8, 700
+    Hq = Hkv * g
+    rng = np.random.default_rng(4242 + exp2)
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t))
+    qf = (rng.standard_normal((B, Hq, 128)) * 2.0 ** exp2).astype(np.float32)
+    q = H.to_device(synth.bf16_bits(qf), "bf16") if qdt == "bf16" else H.to_device(qf, "f32")
+    kcb = H.gpu_book(2, 128)
+    kc = T.CompressedCache.allocate(kcb, B, Hkv, t)
+    T.encode_into_cache(kcb, H.to_device(k.reshape(-1, 128), "bf16"), kc)
+    lens = [t]
+    sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+    _log(f"logits with queries of magnitude 2^{exp2} ({qdt})")
+    got = T.attention_logits(kcb, q, kc, sl, logits=_nan_logits(B, Hq, t))
+    torch.cuda.synchronize()
+    g_np = got.cpu().numpy()
+    assert np.all(np.isfinite(g_np)), "non-finite logits"
+    ref = H.oracle_logits(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), lens,
+                          H.oracle_book(2, 128), g)
+    worst = H.check_logits(g_np, ref, lens)
+    _log(f"  worst relative error {worst:.2e}")
