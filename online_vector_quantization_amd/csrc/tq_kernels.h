@@ -208,7 +208,7 @@ inline bool mdecode_applies(const DecodeArgs &a) {
 hipError_t launch_logits(const DecodeArgs &a, hipStream_t stream);
 // The merge of the chunk kernel's rotated partials (log-sum-exp, Pi_v^T, output).
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t stream);
-// Chunk attention on the matrix cores: query prep, the tiles, the merge.
+// Chunk attention on the matrix cores: the tiles (whose prologue forms q~ and s), the merge.
 hipError_t launch_chunk_mfma(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace tq
