@@ -262,6 +262,10 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, int64_t row0, int
   }
   if constexpr (!SC && (PART & 2) != 0) {
     const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v_codes + row0 * VW);
+    // first tokens of the lane's two groups of four (4 kq .. + 3 of each
+    // half); t_cap is a multiple of 4, so a group lies wholly inside the row
+    // or wholly past it (then it repeats the row's last group, masked later)
+    const int tg0 = min(tb + 4 * kq, last - 3), tg1 = min(tb + 16 + 4 * kq, last - 3);
     if constexpr (SPL) {
       // wide field: 4 W bits from word vw, narrow: 4 N bits from word vn; a
       // 3-bit field may straddle into the next word (read when inside the record)
@@ -270,7 +274,7 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, int64_t row0, int
       const int vw = R::val_wide_bit(n) >> 5, vn = R::val_narrow_bit(n) >> 5;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t tv = static_cast<uint32_t>(min(tb + 16 * (i >> 2) + 4 * kq + (i & 3), last));
+        const uint32_t tv = static_cast<uint32_t>((i < 4 ? tg0 : tg1) + (i & 3));
         const unsigned char *rec = vbase + tv * (VW * 4u);
         r.vf[i][0] = *reinterpret_cast<const uint32_t *>(rec + 4 * vw);
         if constexpr (NWW == 2) r.vf[i][1] = *reinterpret_cast<const uint32_t *>(rec + 4 * vw + 4);
@@ -281,7 +285,7 @@ __device__ __forceinline__ void load_tile(const DecodeArgs &a, int64_t row0, int
       const int w0 = (8 * n * VB) >> 5;   // first word of the lane's value field
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t tv = static_cast<uint32_t>(min(tb + 16 * (i >> 2) + 4 * kq + (i & 3), last));
+        const uint32_t tv = static_cast<uint32_t>((i < 4 ? tg0 : tg1) + (i & 3));
         const uint32_t vo = (tv * VW + w0) * 4u;
         r.vf[i][0] = *reinterpret_cast<const uint32_t *>(vbase + vo);
         if constexpr (VB == 3) r.vf[i][1] = (w0 + 1 < VW) ? *reinterpret_cast<const uint32_t *>(vbase + vo + 4) : 0u;
