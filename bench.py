@@ -55,7 +55,7 @@ ENCODE_COUNTERS = {
                                   "mfma_busy": 0.342, "valu_busy": 0.324},
     "bulk-encode-16777216-kv-then-decode-g8-s262144": {
         "source_sha256": "344bfa705087a3b458f905a3032535374a3a914f393d56501082a3246cd41703",
-        "fetch_bytes": 4296386874, "write_bytes": 1207992640, "mfma_busy": 0.5, "valu_busy": 0.467},
+        "fetch_bytes": 4296388709, "write_bytes": 1207986987, "mfma_busy": 0.497, "valu_busy": 0.464},
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 BULK_NAME = "bulk-encode-16777216-kv-then-decode-g8-s262144"
