@@ -27,17 +27,20 @@
 // large terms; the value sum, whose result only needs absolute accuracy,
 // takes bf16 parts.
 //
-// Work-group = (batch b, kv head, chunk of tokens), 8 waves.  Prologue:
-// q~ and s for the g heads in fp32 (partial dot products reduced in LDS), the
-// query operands split into registers, and three lookup tables in LDS (key
-// codes -> (hi, lo) centroid pairs, sign bytes -> eight +-1, pairs of tokens'
-// value codes -> (hi, lo) centroid pairs).  Main loop: each wave owns every
-// eighth 32-token tile of the chunk, with its own running max, sum and output
-// accumulators, and the next tile's records loaded into registers during the
-// current one.  Per tile and 16-token half: 8 MFMAs give the key term, 4 the
+// Work-group = (batch b, kv head, chunk of tokens), 8 waves.  Prologue: the
+// lookup tables in LDS (key code pairs, or code quads for 1- and 2-bit codes,
+// -> (hi, lo) centroid operands; sign bytes -> eight +-1; pairs of tokens'
+// value codes -> (hi, lo) centroid operands), then q~ and s of the g heads on
+// the matrix cores from fp16 hi/lo fragments of Pi_k and S Pi_k (22-bit
+// operands, fp32-level results), and the query operands split into
+// registers.  Main loop: each wave owns every eighth 32-token tile of the
+// chunk, with its own running max, sum and output accumulators; tile i's
+// value phase and tile i + 1's score phase run in one block while later
+// tiles' records load, and the two waves of a SIMD take turns at a raised
+// priority.  Per tile and 16-token half: 8 MFMAs give the key term, 4 the
 // sign term; the score's two columns are added across lanes, the online
 // softmax (running max raised lazily) forms p nu^v, split hi/lo into the
-// value product's B operand; 16 MFMAs accumulate the value sum.  Epilogue:
+// value product's B operand; 8 MFMAs accumulate the value sum.  Epilogue:
 // the waves merge, Pi_v^T rotates the chunk's sum back, and the work-group
 // writes the output (one chunk per row) or its partial for the merge launch.
 //
@@ -45,9 +48,9 @@
 // kq = l / 16): A operand A[n][8 kq .. 8 kq + 7]; B operand B[8 kq ..][n];
 // result C[4 kq + e][n], e = 0..3.  Here:
 //   scores  C[token][column] = K^(tokens x coords) Q(coords x columns): lane
-//           (n, kq) dequantizes token n's coordinates 32 kq + 8 s .. + 7 at
-//           k-step s (its KB code words in one load) and receives tokens
-//           4 kq + e of every column n;
+//           (n, kq) dequantizes token n's coordinates 32 kq + 4 s .. + 3 at
+//           k-step s, each as its (hi, lo) pair (its KB code words in one
+//           load), and receives tokens 4 kq + e of every column n;
 //   values  C[coord][column] = V^T(coords x tokens) P(tokens x columns): row n
 //           of block cb is coordinate 8 n + cb, so lane (n, kq) dequantizes
 //           coordinates 8 n .. 8 n + 7 (one 8 b'-bit field per token) of the
