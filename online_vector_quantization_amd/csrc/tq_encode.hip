@@ -254,20 +254,22 @@ void pack_encode_fragments(const float *mat, void *dst, bool split_rows, bool sp
 
 bool build_quant_cells(const float *thresholds, const float *centroids, int levels, float *cells,
                        float *qscale, float *qbias) {
-  // Cells of width w = 2/K over [-1, 1]; the kernel computes
-  // cell = min(uint(y * K/2 + K/2), entries - 1) (truncating, negative -> 0,
-  // NaN -> 0).  A rotated unit vector has |y| <= 1 up to rounding, so cells
-  // 0 .. K (K: y at or just above 1) are what occur; the guard entries past K
-  // repeat the last cell.  For each cell: the count of thresholds below (lo - eps), the
-  // single threshold in [lo - eps, hi + eps] (NaN if none) and the centroids
-  // on either side of it.  eps covers the rounding of the cell computation;
-  // more than one candidate fails the build.
+  // Cells of width w = 2/K over [-1, 1] (K = 256); the kernel computes
+  // cell = byte(y * K/2 + K/2 - 1/2) with v_cvt_pk_u8_f32 (round to nearest
+  // even, saturated to 0 .. 255, NaN -> 0): floor(y * K/2 + K/2) except where
+  // y lies exactly on a cell edge, which may give the cell below.  A rotated
+  // unit vector has |y| <= 1 up to rounding; larger or smaller values (a norm
+  // lost to underflow) land in the end cells, which count every threshold or
+  // none.  For each cell: the count of thresholds below (lo - eps), the single
+  // threshold in [lo - eps, hi + eps] (NaN if none) and the centroids on
+  // either side of it.  eps covers the rounding of the cell computation and
+  // the edge case above; more than one candidate fails the build.
   const double w = 2.0 / kQuantCells, eps = 0.05 * w;
   const int nt = levels - 1;
   for (int i = 0; i < nt; ++i)
     if (!(std::fabs(thresholds[i]) < 1.0 - 2 * w)) return false;
   for (int k = 0; k < kQuantCellEntries; ++k) {
-    const double lo = -1.0 + std::min(k, kQuantCells) * w, hi = lo + w;
+    const double lo = -1.0 + k * w, hi = lo + w;
     int below = 0, cand = -1, ncand = 0;
     for (int i = 0; i < nt; ++i) {
       if (thresholds[i] < lo - eps) {
@@ -285,7 +287,7 @@ bool build_quant_cells(const float *thresholds, const float *centroids, int leve
     cells[4 * k + 3] = centroids[std::min(below + 1, levels - 1)];
   }
   *qscale = static_cast<float>(kQuantCells / 2.0);
-  *qbias = static_cast<float>(kQuantCells / 2.0);
+  *qbias = static_cast<float>(kQuantCells / 2.0 - 0.5);
   return true;
 }
 

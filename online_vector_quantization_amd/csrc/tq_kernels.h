@@ -31,10 +31,11 @@ __host__ __device__ constexpr int enc_coord(bool split, int kq, int t, int e) {
 constexpr size_t kFragBytesPerSplit = 8 * 4 * 64 * 16;   // 32 KiB
 constexpr size_t kFragBytes = 2 * kFragBytesPerSplit;     // hi + lo
 
-// Quantizer cell table: kQuantCells cells over [-1, 1] plus guard entries,
-// kQuantCellEntries float4 entries in all (see build_quant_cells).
-constexpr int kQuantCells = 512;
-constexpr int kQuantCellEntries = kQuantCells + 8;
+// Quantizer cell table: kQuantCells cells over [-1, 1], one float4 entry each
+// (see build_quant_cells); the kernel's cell index is one saturating byte
+// conversion, so 256 cells.
+constexpr int kQuantCells = 256;
+constexpr int kQuantCellEntries = kQuantCells;
 
 struct EncodeArgs {
   const void *x;
@@ -58,7 +59,7 @@ struct EncodeArgs {
   const uint4 *frag_qjl;   // kFragBytes (keys with QJL): fragments of -S
   const float4 *qlut;      // kQuantCellEntries quantizer cells
   const float4 *qlut_wide; // split widths: the wide codebook's cells (else null)
-  float qscale, qbias;     // cell = min(uint(y * qscale + qbias), kQuantCellEntries - 1)
+  float qscale, qbias;     // cell = byte(y * qscale + qbias): round to nearest even, saturated to 0 .. 255, NaN -> 0
 };
 
 // Fills `dst` (kFragBytes) with the hi/lo bf16 fragments of the 128 x 128
