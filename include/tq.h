@@ -247,10 +247,11 @@ tq_status tq_decode_attention_static(const tq_codebook *kcb, const tq_codebook *
  * j equals tq_decode_attention of that query alone with seq_len[b] - n_new +
  * j + 1 tokens up to the order of the split sums (bitwise when both launches
  * pick the same token-chunk length).  From 16 query rows per kv head on, the
- * matrix cores compute the query rotation, the scores and the value sum with
- * bf16 hi/lo operand splits (two or three products per fp32 product, about
- * 2^-16 relative error per product); the outputs agree with the single-query
- * path to about 1e-4 (max-abs over unit-scale outputs). */
+ * matrix cores compute the query rotation with fp16 hi/lo operands (22
+ * significant bits) and the scores and the value sum with bf16 hi/lo operand
+ * splits (two or three products per fp32 product, about 2^-16 relative error
+ * per product); the outputs agree with the single-query path to about 1e-4
+ * (max-abs over unit-scale outputs). */
 tq_status tq_chunk_attention(const tq_codebook *kcb, const tq_codebook *vcb, const void *q, tq_dtype q_dtype,
                              const tq_cache *k, const tq_cache *v, const int32_t *seq_len, int32_t batch,
                              int32_t n_q_heads, int32_t n_kv_heads, int32_t n_new, float softmax_scale, void *out,

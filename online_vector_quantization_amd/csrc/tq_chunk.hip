@@ -69,8 +69,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4 mfma16h(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// fp16 hi parts of (a, b) packed (a in the low half), or with lo set their
+// lo parts fp16(a - hi)
+__device__ __forceinline__ uint32_t split_f16(float a, float b, bool lo) {
+  const f16x2 h = __builtin_convertvector((f32x2){a, b}, f16x2);
+  const f16x2 l = __builtin_convertvector((f32x2){a - static_cast<float>(h[0]), b - static_cast<float>(h[1])}, f16x2);
+  return __builtin_bit_cast(uint32_t, lo ? l : h);
 }
 
 // (a, b) rounded to bf16 (nearest even): a in the low half.
@@ -143,8 +152,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
         uint16_t sl[QJL ? kRows * kSStride : 8];   // and lo
         uint16_t qh[kRows * kSStride];             // prologue: q~ as bf16 hi, [row][coordinate]
         uint16_t ql[kRows * kSStride];             // and lo
-        uint16_t xh[kRows * kSStride];             // prologue: the queries as bf16 hi, [row][coordinate]
+        uint16_t xh[kRows * kSStride];             // prologue: the scaled queries as fp16 hi, [row][coordinate]
         uint16_t xl[kRows * kSStride];             // and lo
+        int xexp[kRows];                           // prologue: each row's power-of-two query scale
         uint32_t vst[kWaves][kVst];                // each wave's value records of its step
         float fac[kWaves][3][kStep];               // per token: scale log2(e) nu, coef gamma, nu^v
       } loop;
@@ -198,27 +208,48 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
       sm.sgn[e] = make_uint4(z[0], z[1], z[2], z[3]);
     }
   }
-  // The block's queries into LDS as bf16 hi/lo (thread: row tid / 8,
-  // coordinates 16 (tid % 8) .. + 15; rows past the last read as zero).
+  // The block's queries into LDS as fp16 hi/lo of 2^x q, x per row bringing
+  // the row's largest |q| into [64, 128) (thread: row tid / 8, coordinates
+  // 16 (tid % 8) .. + 15, the row's eight threads adjacent lanes; rows past
+  // the last read as zero; a bf16 query has no lo part).
   const bool q_bf16 = a.q_bf16 != 0;
   {
     const int r = tid >> 3, c0 = 16 * (tid & 7);
     const int m = m0 + r;
-    uint32_t h[8], l[8];
+    float qv[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) h[k] = l[k] = 0u;
+    for (int k = 0; k < 16; ++k) qv[k] = 0.f;
     if (m < rows_total) {
       const int64_t qi = (static_cast<int64_t>(b * a.n_q_heads + hk * g + m % g) * a.n_new + m / g) * D + c0;
       // 4-byte reads: the query need only be 4-byte aligned
       if (q_bf16) {
         const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(a.q) + qi);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) h[k] = src[k];
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t w = src[k];
+          qv[2 * k] = __uint_as_float(w << 16);
+          qv[2 * k + 1] = __uint_as_float(w & 0xffff0000u);
+        }
       } else {
         const float *src = static_cast<const float *>(a.q) + qi;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) split_pair(src[2 * k], src[2 * k + 1], h[k], l[k]);
+        for (int k = 0; k < 16; ++k) qv[k] = src[k];
       }
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fabsf(qv[k]));
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    int ex = 0;
+    (void)frexpf(mx, &ex);
+    const int xe = (mx > 0.f && mx < INFINITY) ? 7 - ex : 0;
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float y0 = ldexpf(qv[2 * k], xe), y1 = ldexpf(qv[2 * k + 1], xe);
+      h[k] = split_f16(y0, y1, false);
+      l[k] = split_f16(y0, y1, true);
     }
     uint4 *dh = reinterpret_cast<uint4 *>(&sm.u.loop.xh[r * kSStride + c0]);
     uint4 *dl = reinterpret_cast<uint4 *>(&sm.u.loop.xl[r * kSStride + c0]);
@@ -226,71 +257,71 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(DecodeArgs a) {
     dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
     dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
     dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+    if ((tid & 7) == 0) sm.u.loop.xexp[r] = xe;
   }
-  // q~ = Pi_k q and s = S q~ of the block's rows on the matrix cores
-  // (v_mfma_f32_16x16x32_bf16), from the codebook's bf16 hi/lo operand
-  // fragments of Pi_k and of -S: wave t takes output tile t, whose lane
-  // (n, kq) receives coordinates 32 kq + 4 t .. + 3 of row n of an N-block,
-  // and reads each fragment once.  B operand: lane (n, kq), element e of
-  // k-step ks = input coordinate 32 kq + 8 ks + e of row n.  The products
-  // take the passes hi*hi + lo*hi (+ hi*lo for fp32 queries and for q~).
+  // q~ = Pi_k q and s = S Pi_k q of the block's rows on the matrix cores
+  // (v_mfma_f32_16x16x32_f16), from the codebook's fp16 hi/lo fragments of
+  // 2^kDecFragExp Pi_k and 2^kDecFragExp S Pi_k (the encode's layout): wave t
+  // takes output tile t of both, whose lane (n, kq) receives coordinates
+  // 32 kq + 4 t .. + 3 of row n of an N-block, and reads each fragment once.
+  // B operand: lane (n, kq), element e of k-step ks = query coordinate
+  // 32 kq + 8 ks + e of row n.  The passes hi*hi + lo*hi (+ hi*lo for fp32
+  // queries) keep 22 significant bits of either operand; q~ and s are then
+  // split into the bf16 hi/lo operands of the scores.
   const int n16 = lane & 15, kq4 = lane >> 4;
-  const uint4 *fr = a.k_frag_rot;
-  bf16x8 fa_h[4], fa_l[4];
+  f16x8 ph[4], pl[4], fsh[QJL ? 4 : 1], fsl[QJL ? 4 : 1];
+  {
+    const uint4 *fr = a.k_dfrag_rot;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    fa_h[ks] = __builtin_bit_cast(bf16x8, fr[((0 * 8 + wave) * 4 + ks) * 64 + lane]);
-    fa_l[ks] = __builtin_bit_cast(bf16x8, fr[((1 * 8 + wave) * 4 + ks) * 64 + lane]);
+    for (int ks = 0; ks < 4; ++ks) {
+      ph[ks] = __builtin_bit_cast(f16x8, fr[((0 * 8 + wave) * 4 + ks) * 64 + lane]);
+      pl[ks] = __builtin_bit_cast(f16x8, fr[((1 * 8 + wave) * 4 + ks) * 64 + lane]);
+    }
+    if constexpr (QJL) {
+      const uint4 *fq = a.k_dfrag_qjl;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        fsh[ks] = __builtin_bit_cast(f16x8, fq[((0 * 8 + wave) * 4 + ks) * 64 + lane]);
+        fsl[ks] = __builtin_bit_cast(f16x8, fq[((1 * 8 + wave) * 4 + ks) * 64 + lane]);
+      }
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int nb = 0; nb < kRows / 16; ++nb) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 aq = {0.f, 0.f, 0.f, 0.f}, as = aq;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int xo = (16 * nb + n16) * kSStride + 32 * kq4 + 8 * ks;
-      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&sm.u.loop.xh[xo]);
-      acc = mfma16(fa_h[ks], bh, acc);
-      acc = mfma16(fa_l[ks], bh, acc);
-      if (!q_bf16) acc = mfma16(fa_h[ks], *reinterpret_cast<const bf16x8 *>(&sm.u.loop.xl[xo]), acc);
+      const f16x8 bh = *reinterpret_cast<const f16x8 *>(&sm.u.loop.xh[xo]);
+      aq = mfma16h(ph[ks], bh, aq);
+      aq = mfma16h(pl[ks], bh, aq);
+      if constexpr (QJL) {
+        as = mfma16h(fsh[ks], bh, as);
+        as = mfma16h(fsl[ks], bh, as);
+      }
+      if (!q_bf16) {
+        const f16x8 bl = *reinterpret_cast<const f16x8 *>(&sm.u.loop.xl[xo]);
+        aq = mfma16h(ph[ks], bl, aq);
+        if constexpr (QJL) as = mfma16h(fsh[ks], bl, as);
+      }
     }
-    uint32_t h0, l0, h1, l1;
-    split_pair(acc[0], acc[1], h0, l0);
-    split_pair(acc[2], acc[3], h1, l1);
+    // undo the operands' scales 2^kDecFragExp and 2^x of the row
+    const float un = ldexpf(1.f, -(kDecFragExp + sm.u.loop.xexp[16 * nb + n16]));
     const int qo = (16 * nb + n16) * kSStride + 32 * kq4 + 4 * wave;
+    uint32_t h0, l0, h1, l1;
+    split_pair(aq[0] * un, aq[1] * un, h0, l0);
+    split_pair(aq[2] * un, aq[3] * un, h1, l1);
     *reinterpret_cast<uint2 *>(&sm.u.loop.qh[qo]) = make_uint2(h0, h1);
     *reinterpret_cast<uint2 *>(&sm.u.loop.ql[qo]) = make_uint2(l0, l1);
-  }
-  if constexpr (QJL) {
-    const uint4 *fq = a.k_frag_qjl;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      fa_h[ks] = __builtin_bit_cast(bf16x8, fq[((0 * 8 + wave) * 4 + ks) * 64 + lane]);
-      fa_l[ks] = __builtin_bit_cast(bf16x8, fq[((1 * 8 + wave) * 4 + ks) * 64 + lane]);
+    if constexpr (QJL) {
+      split_pair(as[0] * un, as[1] * un, h0, l0);
+      split_pair(as[2] * un, as[3] * un, h1, l1);
+      *reinterpret_cast<uint2 *>(&sm.u.loop.sh[qo]) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2 *>(&sm.u.loop.sl[qo]) = make_uint2(l0, l1);
     }
   }
   __syncthreads();
-  if constexpr (QJL) {
-#pragma unroll
-    for (int nb = 0; nb < kRows / 16; ++nb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int xo = (16 * nb + n16) * kSStride + 32 * kq4 + 8 * ks;
-        const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&sm.u.loop.qh[xo]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&sm.u.loop.ql[xo]);
-        acc = mfma16(fa_h[ks], bh, acc);
-        acc = mfma16(fa_l[ks], bh, acc);
-        acc = mfma16(fa_h[ks], bl, acc);
-      }
-      uint32_t h0, l0, h1, l1;   // the fragments hold -S
-      split_pair(-acc[0], -acc[1], h0, l0);
-      split_pair(-acc[2], -acc[3], h1, l1);
-      const int so = (16 * nb + n16) * kSStride + 32 * kq4 + 4 * wave;
-      *reinterpret_cast<uint2 *>(&sm.u.loop.sh[so]) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2 *>(&sm.u.loop.sl[so]) = make_uint2(l0, l1);
-    }
-  }
   // B operands of the scores: row m0 + 32 mh + l32, coordinates 64 hi + 8 ks .. + 7 of q~
   const int mrow = m0 + 32 * mh + l32;
   const bool row_live = mrow < rows_total;
@@ -634,8 +665,8 @@ hipError_t launch_chunk_mfma(const DecodeArgs &a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
   const int n_mb = (g * a.n_new + kRows - 1) / kRows;
   if (a.n_chunks > kMaxDecodeChunks || a.v_bits < 1 || a.v_bits > 4 || a.n_new < 1 || g < 1 || g > 8 || a.k_split ||
-      static_cast<int64_t>(a.n_kv_heads) * n_mb > 65535 || a.k_frag_rot == nullptr ||
-      (a.qjl_m > 0 && a.k_frag_qjl == nullptr))
+      static_cast<int64_t>(a.n_kv_heads) * n_mb > 65535 || a.k_dfrag_rot == nullptr ||
+      (a.qjl_m > 0 && a.k_dfrag_qjl == nullptr))
     return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
   const dim3 grid(a.n_chunks, a.n_kv_heads * n_mb, a.batch);
