@@ -51,8 +51,8 @@ HBM_PEAK_GBPS = 8000.0
 # SQ_ACTIVE_INST_VALU less MFMA instructions at 4 cycles each).
 ENCODE_COUNTERS = {
     "llama3-8b-layer-b1-s32768": {"source_sha256": "0fb2c28e80e28c44fb70d9e4820a5eba23996484616e42e6596d21ee0c46fb99",
-                                  "fetch_bytes": 68462818, "write_bytes": 14702384,
-                                  "mfma_busy": 0.348, "valu_busy": 0.311},
+                                  "fetch_bytes": 68462247, "write_bytes": 14698483,
+                                  "mfma_busy": 0.352, "valu_busy": 0.315},
     "bulk-encode-16777216-kv-then-decode-g8-s262144": {
         "source_sha256": "0fb2c28e80e28c44fb70d9e4820a5eba23996484616e42e6596d21ee0c46fb99",
         "fetch_bytes": 4296334737, "write_bytes": 1208018197, "mfma_busy": 0.513, "valu_busy": 0.453},
