@@ -70,6 +70,14 @@ __device__ __forceinline__ uint32_t shift_in_sign(uint32_t w, float np) {
   return __builtin_amdgcn_alignbit(w, __float_as_uint(np), 31);
 }
 
+// y - c rounded on its own, never fused with the product that formed y: the
+// residual is the same in every instantiation (with and without the debug
+// outputs, which keep y), so the sign bits are too.
+__device__ __forceinline__ float sub_unfused(float y, float c) {
+#pragma clang fp contract(off)
+  return y - c;
+}
+
 // Round 8 floats to bf16 (RNE) and return hi and lo = bf16(v - hi).
 // The rounded pairs are unpacked back to fp32 with a shift and a mask (the
 // generic conversion would round each element a second time).
@@ -108,20 +116,24 @@ template <bool XF32> struct XRegs;
 template <> struct XRegs<false> { uint4 w[4]; };
 template <> struct XRegs<true> { float4 w[8]; };
 
+// Columns past the last vector (n >= 1 whenever a tile exists) read the last
+// vector again: every load stays in bounds with no predication, and nothing
+// computed for those columns is stored.  MFMA columns, the norm's lane
+// exchange (lanes of one vector) and the emit never mix columns.
 template <bool XF32, int NT>
 __device__ __forceinline__ void load_x(const EncodeArgs &a, int64_t tile, int j, int kk, XRegs<XF32> (&x)[NT]) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int64_t vec = tile * (16 * NT) + nt * 16 + j;
-    const bool valid = vec < a.n;
+    const int64_t row = vec < a.n ? vec : a.n - 1;
     if constexpr (!XF32) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + vec * a.x_stride + 32 * kk);
+      const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + row * a.x_stride + 32 * kk);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) x[nt].w[s] = valid ? src[s] : make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < 4; ++s) x[nt].w[s] = src[s];
     } else {
-      const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + vec * a.x_stride + 32 * kk);
+      const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + row * a.x_stride + 32 * kk);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) x[nt].w[s] = valid ? src[s] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < 8; ++s) x[nt].w[s] = src[s];
     }
   }
 }
