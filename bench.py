@@ -50,12 +50,12 @@ HBM_PEAK_GBPS = 8000.0
 # busy fractions (SQ_VALU_MFMA_BUSY_CYCLES over 1,024 SIMDs x kernel cycles;
 # SQ_ACTIVE_INST_VALU less MFMA instructions at 4 cycles each).
 ENCODE_COUNTERS = {
-    "llama3-8b-layer-b1-s32768": {"source_sha256": "0fb2c28e80e28c44fb70d9e4820a5eba23996484616e42e6596d21ee0c46fb99",
-                                  "fetch_bytes": 68462247, "write_bytes": 14698483,
-                                  "mfma_busy": 0.352, "valu_busy": 0.315},
+    "llama3-8b-layer-b1-s32768": {"source_sha256": "f269781c809e695b78f22dc19bcf980778589bc3391b7e82d966e6b377c8f8fc",
+                                  "fetch_bytes": 68436769, "write_bytes": 14683847,
+                                  "mfma_busy": 0.358, "valu_busy": 0.291},
     "bulk-encode-16777216-kv-then-decode-g8-s262144": {
-        "source_sha256": "0fb2c28e80e28c44fb70d9e4820a5eba23996484616e42e6596d21ee0c46fb99",
-        "fetch_bytes": 4296334737, "write_bytes": 1208018197, "mfma_busy": 0.513, "valu_busy": 0.453},
+        "source_sha256": "f269781c809e695b78f22dc19bcf980778589bc3391b7e82d966e6b377c8f8fc",
+        "fetch_bytes": 4296303039, "write_bytes": 1207996693, "mfma_busy": 0.530, "valu_busy": 0.427},
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 BULK_NAME = "bulk-encode-16777216-kv-then-decode-g8-s262144"
