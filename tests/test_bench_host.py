@@ -59,3 +59,20 @@ def test_key_encode_mfma_flops(bench):
 def test_sub_record_drops_headline_keys(bench):
     line = {"metric": "m", "value": 1.0, "unit": "GB/s", "config": {"workload": "w"}, "steps": 3}
     assert bench.sub_record(line) == {"value": 1.0, "config": {"workload": "w"}}
+
+
+def test_committed_counters_are_the_committed_profiles(bench):
+    # the encode counters the bench line reports were taken on these sources,
+    # and are the figures of the committed byte-counter summaries
+    sha = bench.encode_source_sha256()
+    summaries = {"llama3-8b-layer-b1-s32768": "encode_decode_llama8b_hbm_counters.md",
+                 bench.BULK_NAME: "encode_decode_bulk_hbm_counters.md"}
+    assert set(bench.ENCODE_COUNTERS) == set(summaries)
+    for wl, t in bench.ENCODE_COUNTERS.items():
+        assert t["source_sha256"] == sha, f"{wl}: counters taken on other encode sources"
+        text = open(os.path.join(ROOT, "profiles", summaries[wl])).read()
+        assert sha in text
+        assert f"Key encode: {t['fetch_bytes'] / 1e6:.3f} MB read + {t['write_bytes'] / 1e6:.3f} MB written" in text
+        issue = open(os.path.join(ROOT, "profiles", summaries[wl].replace("hbm", "issue"))).read()
+        row = [r for r in issue.splitlines() if r.startswith("| encode keys") and r.count("|") > 8]
+        assert len(row) == 1 and f"| {100 * t['mfma_busy']:.1f} | {100 * t['valu_busy']:.1f} |" in row[0]
