@@ -38,7 +38,7 @@ def test_encode_tiny_config_fp32_keys():
     cb = H.gpu_book(2, 128)
     got = H.encode_gpu(cb, H.to_device(x, "f32"))
     flips = H.check_encode(x, got, 2, 128)
-    # Codes/signs are judged bit-exactly on the GPU's own fp32 values above; against the
+    # Codes/signs are checked bit-exactly on the GPU's own fp32 values above; against the
     # oracle's float64 values only decisions within rounding of a threshold (or of p = 0)
     # may differ: a handful in 10^6.
     _log(f"near-boundary flips vs float64 oracle: {flips} of {x.shape[0] * 256}")
