@@ -76,3 +76,12 @@ def test_committed_counters_are_the_committed_profiles(bench):
         issue = open(os.path.join(ROOT, "profiles", summaries[wl].replace("hbm", "issue"))).read()
         row = [r for r in issue.splitlines() if r.startswith("| encode keys") and r.count("|") > 8]
         assert len(row) == 1 and f"| {100 * t['mfma_busy']:.1f} | {100 * t['valu_busy']:.1f} |" in row[0]
+
+
+def test_more_than_one_gpu_is_refused():
+    # one GPU only: any other count exits with a message before touching a device
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
