@@ -96,6 +96,36 @@ def test_chunk_parity(kbits, m, vbits, g, n_new, qdt):
     assert np.all(g_np[1, :, :empty] == 0.0)
 
 
+@pytest.mark.parametrize("exp2,qdt", [(60, "bf16"), (-60, "bf16"), (40, "f32"), (-40, "f32")])
+def test_chunk_query_magnitude_extremes(exp2, qdt):
+    """The matrix-core tiles scale each query row by a power of two into fp16
+    range before the query rotation: queries 2^+-60 (bf16) and 2^+-40 (fp32)
+    give finite outputs within the oracle's bar (near one-hot softmax for the
+    large ones, near uniform for the small ones)."""
+    B, Hkv, g, n_new, t = 1, 2, 4, 16, 700
+    Hq = Hkv * g
+    rng = np.random.default_rng(5151 + abs(exp2) + (qdt == "f32"))
+    k = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t))
+    v = synth.bf16_bits(synth.kv_block(rng, B, Hkv, t))
+    qf = (rng.standard_normal((B, Hq, n_new, 128)) * 2.0 ** exp2).astype(np.float32)
+    q = H.to_device(synth.bf16_bits(qf), "bf16") if qdt == "bf16" else H.to_device(qf, "f32")
+    kcb, vcb = H.gpu_book(2, 128), H.gpu_book(3, 0)
+    assert T.api.chunk_uses_mfma(g, n_new)
+    kc, vc = H.build_cache(kcb, vcb, H.to_device(k, "bf16"), H.to_device(v, "bf16"), B, Hkv, t, t)
+    lens = [t]
+    sl = torch.tensor(lens, dtype=torch.int32, device=H.DEV)
+    _log(f"chunk with queries of magnitude 2^{exp2} ({qdt})")
+    got = T.chunk_attention(kcb, vcb, q, kc, vc, sl)
+    torch.cuda.synchronize()
+    g_np = got.cpu().numpy()
+    assert np.all(np.isfinite(g_np)), "non-finite outputs"
+    ref = O.chunk_attention(q.float().cpu().numpy().astype(np.float64), H.cache_to_host(kc), H.cache_to_host(vc),
+                            lens, H.oracle_book(2, 128), H.oracle_book(3, 0))
+    err = np.abs(g_np - ref).max()
+    _log(f"  vs oracle: max-abs {err:.2e}")
+    assert err <= 2e-3, f"max-abs error {err:.3e}"
+
+
 def test_chunk_bf16_output_and_determinism():
     B, Hkv, g, n_new, t_cap = 2, 2, 4, 7, 900
     rng = np.random.default_rng(5)
