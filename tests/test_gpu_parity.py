@@ -100,17 +100,22 @@ def test_encode_zero_nan_inf_vectors():
     H.check_encode(x[4:], {k: v[4:] for k, v in got.items()}, 2, 128)
 
 
-@pytest.mark.parametrize("scale_exp", [-55, 40])
-def test_encode_tiny_and_huge_norms(scale_exp):
-    # bf16 vectors scaled by 2^-55 (the squared norm, about 2^-103, lies below
-    # the range where the hardware square root is taken directly) and by 2^40;
-    # the scaling is exact, so the oracle sees the same inputs
+@pytest.mark.parametrize("scale_exp,dt", [(-55, "bf16"), (40, "bf16"), (-58, "f32"), (50, "f32")])
+def test_encode_tiny_and_huge_norms(scale_exp, dt):
+    # vectors scaled by 2^-55 or 2^-58 (the squared norm, about 2^-103 or
+    # 2^-109, lies below the range where the hardware square root is taken
+    # directly) and by 2^40 or 2^50; the oracle sees the same stored inputs
     x = np.random.default_rng(11 + abs(scale_exp)).standard_normal((100, 128)).astype(np.float32)
-    xb = synth.bf16_bits(np.ldexp(x, scale_exp).astype(np.float32))
-    _log(f"encode norms near 2^{scale_exp + 3.5}")
+    xs = np.ldexp(x, scale_exp).astype(np.float32)
+    _log(f"encode {dt} norms near 2^{scale_exp + 3.5}")
     cb = H.gpu_book(3, 128)
-    got = H.encode_gpu(cb, H.to_device(xb, "bf16"))
-    H.check_encode(H.host_values(xb, "bf16"), got, 3, 128)
+    if dt == "bf16":
+        xb = synth.bf16_bits(xs)
+        got = H.encode_gpu(cb, H.to_device(xb, "bf16"))
+        H.check_encode(H.host_values(xb, "bf16"), got, 3, 128)
+    else:
+        got = H.encode_gpu(cb, H.to_device(xs, "f32"))
+        H.check_encode(xs, got, 3, 128)
 
 
 def test_encode_dst_row_scatter_skips_out_of_range():
