@@ -50,12 +50,12 @@ HBM_PEAK_GBPS = 8000.0
 # busy fractions (SQ_VALU_MFMA_BUSY_CYCLES over 1,024 SIMDs x kernel cycles;
 # SQ_ACTIVE_INST_VALU less MFMA instructions at 4 cycles each).
 ENCODE_COUNTERS = {
-    "llama3-8b-layer-b1-s32768": {"source_sha256": "31a494d754c4aaf7290c17c7099d1d9e0cbe92083f02309ba62a28f0511c78d9",
-                                  "fetch_bytes": 68449652, "write_bytes": 14684935,
-                                  "mfma_busy": 0.356, "valu_busy": 0.292},
+    "llama3-8b-layer-b1-s32768": {"source_sha256": "dbc0a21f4aafaee72542cda413bf4dcc80614cb20008847cb481c01614e335c1",
+                                  "fetch_bytes": 68445280, "write_bytes": 14694704,
+                                  "mfma_busy": 0.368, "valu_busy": 0.302},
     "bulk-encode-16777216-kv-then-decode-g8-s262144": {
-        "source_sha256": "31a494d754c4aaf7290c17c7099d1d9e0cbe92083f02309ba62a28f0511c78d9",
-        "fetch_bytes": 4296284053, "write_bytes": 1207990379, "mfma_busy": 0.522, "valu_busy": 0.424},
+        "source_sha256": "dbc0a21f4aafaee72542cda413bf4dcc80614cb20008847cb481c01614e335c1",
+        "fetch_bytes": 4296307135, "write_bytes": 1207991552, "mfma_busy": 0.557, "valu_busy": 0.453},
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 BULK_NAME = "bulk-encode-16777216-kv-then-decode-g8-s262144"
