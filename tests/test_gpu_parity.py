@@ -118,6 +118,27 @@ def test_encode_tiny_and_huge_norms(scale_exp, dt):
         H.check_encode(xs, got, 3, 128)
 
 
+@pytest.mark.parametrize("bits,m,dt", [(1, 128, "bf16"), (2, 128, "bf16"), (3, 128, "bf16"), (3, 128, "f32"),
+                                        (4, 0, "bf16")])
+def test_encode_debug_instantiation_equals_hot_path(bits, m, dt):
+    # The launch with debug outputs (y and p kept) is a separate kernel
+    # instantiation; its codes, signs and norms must be the hot path's bit for
+    # bit over many vectors, including the sign bits whose p lies within
+    # rounding of zero (the residual is formed the same way in both).
+    n = 1 << 18
+    x = torch.randn(n, 128, generator=torch.Generator(device=H.DEV).manual_seed(77 + bits + m), device=H.DEV)
+    x = x.to(torch.bfloat16) if dt == "bf16" else x.contiguous()
+    cb = H.gpu_book(bits, m)
+    _log(f"encode {n} {dt} vectors, bits={bits} m={m}: hot path against the debug instantiation")
+    hot = H.encode_gpu(cb, x, debug=False)
+    dbg = H.encode_gpu(cb, x, debug=True)
+    np.testing.assert_array_equal(hot["codes"], dbg["codes"])
+    np.testing.assert_array_equal(hot["norms"].view(np.uint32), dbg["norms"].view(np.uint32))
+    if m:
+        np.testing.assert_array_equal(hot["signs"], dbg["signs"])
+        np.testing.assert_array_equal(hot["res_norms"].view(np.uint32), dbg["res_norms"].view(np.uint32))
+
+
 def test_encode_dst_row_scatter_skips_out_of_range():
     n, rows = 300, 512
     rng = np.random.default_rng(9)
